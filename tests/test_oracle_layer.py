@@ -1,0 +1,350 @@
+"""Pins for the oracle's permute, FP8 quantisers, expert FFN, combine, bias update and
+whole-layer forward.
+
+References used here are independent of the oracle's loops: numpy's stable argsort
+and bincount, float64 numpy matmuls, torch's CPU dtype conversions, exact dyadic
+arithmetic and closed forms.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+F32 = np.float32
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_route(rng, T, E, K):
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    return idx
+
+
+# --------------------------------------------------------------------------- permute
+
+@pytest.mark.parametrize("T,E,K", [(1, 4, 1), (50, 16, 4), (130, 32, 8), (64, 256, 8)])
+def test_permute_structure(orc, T, E, K):
+    rng = np.random.default_rng(T + E)
+    H = 32
+    x = rng.standard_normal((T, H)).astype(F32)
+    idx = rand_route(rng, T, E, K)
+    if E > 8:
+        idx[idx == 3] = (idx[idx == 3] + 0)  # keep; some experts get no tokens below
+    counts = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+    off, st, inv, xs, xsc = orc.permute(x, idx, counts, E, shared=1)
+    assert xsc is None
+    assert off[0] == 0 and off[E] == T * K and off[E + 1] == T * K + T
+    assert np.array_equal(np.diff(off[:E + 1]), counts)
+    # the rows of the (t,k) pairs in expert-major, token-ascending order
+    e_flat = idx.ravel().astype(np.int64)
+    t_flat = np.repeat(np.arange(T), K)
+    order = np.argsort(e_flat * T + t_flat, kind="stable")
+    assert np.array_equal(st[:T * K], t_flat[order])
+    expect_inv = np.empty(T * K, np.int64)
+    expect_inv[order] = np.arange(T * K)
+    assert np.array_equal(inv.ravel(), expect_inv)
+    for t in range(T):
+        for k in range(K):
+            r = inv[t, k]
+            assert st[r] == t and off[idx[t, k]] <= r < off[idx[t, k] + 1]
+    assert np.array_equal(st[T * K:], np.arange(T))
+    assert np.array_equal(xs, x[st])
+
+
+def test_permute_empty_experts_and_no_shared(orc):
+    T, E, K, H = 10, 8, 2, 16
+    idx = np.tile(np.array([[5, 1]], np.int32), (T, 1))  # only experts 1 and 5 used
+    counts = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+    x = np.arange(T * H, dtype=F32).reshape(T, H)
+    off, st, inv, xs, _ = orc.permute(x, idx, counts, E, shared=0)
+    assert off.tolist() == [0, 0, 10, 10, 10, 10, 20, 20, 20]
+    assert np.array_equal(inv[:, 1], np.arange(T)) and np.array_equal(inv[:, 0], 10 + np.arange(T))
+    assert xs.shape == (T * K, H)
+
+
+def test_permute_rejects_inconsistent_counts(orc):
+    x = np.zeros((4, 16), F32)
+    idx = np.zeros((4, 1), np.int32)
+    with pytest.raises(ValueError):
+        orc.permute(x, idx, np.array([3, 0], np.int32), 2)
+
+
+# --------------------------------------------------------------------------- fp8 quantisers
+
+def test_quantize_act_tiles(orc):
+    rng = np.random.default_rng(3)
+    a = (rng.standard_normal((6, 384)) * rng.uniform(0.001, 100, (6, 1))).astype(F32)
+    a[2, 128:256] = 0.0                   # an all-zero tile gets scale 1 and zero codes
+    q, s = orc.quantize_act_fp8(a)
+    assert s.shape == (6, 3) and s[2, 1] == 1.0 and not q[2, 128:256].any()
+    for r in range(6):
+        for c in range(3):
+            tile = a[r, c * 128:(c + 1) * 128]
+            amax = F32(np.abs(tile).max())
+            if amax == 0:
+                continue
+            assert s[r, c] == F32(amax / F32(448.0))
+            # the tile maximum maps to (about) the largest finite code
+            j = int(np.abs(tile).argmax())
+            assert (q[r, c * 128 + j] & 0x7F) == 0x7E
+            # codes are torch's RNE cast of the fp32 quotient
+            quot = np.clip((tile / s[r, c]).astype(F32), -448, 448)
+            ref = torch.from_numpy(quot).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(q[r, c * 128:(c + 1) * 128], ref)
+            deq = torch.from_numpy(q[r, c * 128:(c + 1) * 128].copy()).view(
+                torch.float8_e4m3fn).float().numpy() * s[r, c]
+            big = np.abs(tile) > amax * 2.0 ** -6
+            assert np.all(np.abs(deq - tile)[big] <= np.abs(tile)[big] * 2.0 ** -4 * 1.0001)
+
+
+def test_quantize_weight_blocks(orc):
+    rng = np.random.default_rng(4)
+    w = orc.bf16_from_f64_array(rng.standard_normal((256, 384)) * 0.006)
+    w = w.reshape(256, 384)
+    q, s = orc.quantize_weight_fp8(w)
+    wf = orc.bf16_to_f32(w)
+    assert s.shape == (2, 3)
+    for i in range(2):
+        for j in range(3):
+            blk = wf[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+            assert s[i, j] == F32(F32(np.abs(blk).max()) / F32(448.0))
+            quot = np.clip((blk / s[i, j]).astype(F32), -448, 448)
+            ref = torch.from_numpy(np.ascontiguousarray(quot)).to(torch.float8_e4m3fn).view(
+                torch.uint8).numpy()
+            assert np.array_equal(q[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128], ref)
+
+
+def test_permute_fp8_rows_carry_token_codes(orc):
+    rng = np.random.default_rng(5)
+    T, H, E, K = 20, 256, 8, 2
+    x = orc.bf16_from_f64_array(rng.standard_normal((T, H))).reshape(T, H)
+    idx = rand_route(rng, T, E, K)
+    counts = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+    off, st, inv, xs, xsc = orc.permute(x, idx, counts, E, shared=1, out_dtype=orc.E4M3)
+    qx, sx = orc.quantize_act_fp8(x)
+    assert np.array_equal(xs, qx[st]) and np.array_equal(xsc, sx[st])
+
+
+# --------------------------------------------------------------------------- expert FFN
+
+def swiglu_f64(x, w13, w2, I):
+    a = x @ w13[:I].T
+    u = x @ w13[I:].T
+    return a / (1.0 + np.exp(-a)) * u
+
+
+def test_ffn_f32_against_float64_numpy(orc):
+    rng = np.random.default_rng(6)
+    n, H, I = 9, 256, 128
+    x = rng.standard_normal((n, H)).astype(F32)
+    w13 = (rng.standard_normal((2 * I, H)) * 0.05).astype(F32)
+    w2 = (rng.standard_normal((H, I)) * 0.05).astype(F32)
+    y = orc.expert_ffn(x, w13, w2, orc.F32)
+    h = swiglu_f64(x.astype(np.float64), w13.astype(np.float64), w2, I).astype(F32)
+    ref = h.astype(np.float64) @ w2.astype(np.float64).T
+    assert np.abs(y - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
+def test_ffn_bf16_against_float64_numpy(orc):
+    rng = np.random.default_rng(7)
+    n, H, I = 5, 256, 128
+    xb = orc.bf16_from_f64_array(rng.standard_normal((n, H))).reshape(n, H)
+    w13b = orc.bf16_from_f64_array(rng.standard_normal((2 * I, H)) * 0.05).reshape(2 * I, H)
+    w2b = orc.bf16_from_f64_array(rng.standard_normal((H, I)) * 0.05).reshape(H, I)
+    y = orc.expert_ffn(xb, w13b, w2b, orc.BF16)
+    x, w13, w2 = (orc.bf16_to_f32(v).astype(np.float64) for v in (xb, w13b, w2b))
+    h = swiglu_f64(x, w13, w2, I)
+    hb = torch.from_numpy(h).to(torch.bfloat16).double().numpy()
+    ref = hb @ w2.T
+    yf = orc.bf16_to_f32(y).astype(np.float64)
+    # h may land on the other side of a bf16 rounding boundary (torch rounds via
+    # float32); Y is within a bf16 ulp plus that effect
+    assert np.abs(yf - ref).max() <= 2 ** -7 * np.abs(ref).max()
+    assert np.mean(np.abs(yf - ref) <= np.abs(ref) * 2 ** -8 + 1e-12) > 0.99
+
+
+def test_ffn_closed_forms(orc):
+    rng = np.random.default_rng(8)
+    n, H, I = 3, 128, 128
+    x = rng.standard_normal((n, H)).astype(F32)
+    w13 = rng.standard_normal((2 * I, H)).astype(F32)
+    w2 = rng.standard_normal((H, I)).astype(F32)
+    assert not orc.expert_ffn(x, w13, np.zeros_like(w2), orc.F32).any()
+    g0 = w13.copy(); g0[:I] = 0       # gate projection zero -> silu(0) = 0 -> h = 0
+    assert not orc.expert_ffn(x, g0, w2, orc.F32).any()
+    u0 = w13.copy(); u0[I:] = 0       # up projection zero -> h = 0
+    assert not orc.expert_ffn(x, u0, w2, orc.F32).any()
+    # gate and up are not interchangeable
+    sw = np.concatenate([w13[I:], w13[:I]])
+    assert not np.allclose(orc.expert_ffn(x, sw, w2, orc.F32), orc.expert_ffn(x, w13, w2, orc.F32))
+
+
+def test_ffn_fp8_against_dequantised_float64(orc):
+    rng = np.random.default_rng(9)
+    n, H, I = 4, 256, 256
+    xb = orc.bf16_from_f64_array(rng.standard_normal((n, H))).reshape(n, H)
+    w13b = orc.bf16_from_f64_array(rng.standard_normal((2 * I, H)) * 0.006).reshape(2 * I, H)
+    w2b = orc.bf16_from_f64_array(rng.standard_normal((H, I)) * 0.006).reshape(H, I)
+    qx, sx = orc.quantize_act_fp8(xb)
+    q13, s13 = orc.quantize_weight_fp8(w13b)
+    q2, s2 = orc.quantize_weight_fp8(w2b)
+    y = orc.expert_ffn(qx, q13, q2, orc.BF16, sx, s13, s2)
+
+    def deq(q):
+        return torch.from_numpy(np.ascontiguousarray(q)).view(torch.float8_e4m3fn).double().numpy()
+
+    xd = deq(qx) * np.repeat(sx, 128, axis=1)
+    w13d = deq(q13) * np.kron(s13, np.ones((128, 128)))
+    w2d = deq(q2) * np.kron(s2, np.ones((128, 128)))
+    h = swiglu_f64(xd, w13d, w2d, I).astype(F32)
+    qh, sh = orc.quantize_act_fp8(h)
+    hd = deq(qh) * np.repeat(sh, 128, axis=1)
+    ref = hd @ w2d.T
+    yf = orc.bf16_to_f32(y).astype(np.float64)
+    assert np.abs(yf - ref).max() <= 2 ** -8 * np.abs(ref).max()
+
+
+# --------------------------------------------------------------------------- combine
+
+def test_combine_identity_experts(orc):
+    rng = np.random.default_rng(10)
+    T, H, E, K = 40, 64, 16, 4
+    x = rng.standard_normal((T, H)).astype(F32)
+    z = rng.standard_normal((T, E)).astype(F32)
+    idx, gate, counts = orc.select(z, np.zeros(E, F32), 4, 2, K, 2)
+    off, st, inv, xs, _ = orc.permute(x, idx, counts, E, shared=1)
+    ys = xs.copy()
+    ys[T * K:] = 0.0                  # shared expert contributes nothing
+    y = orc.combine(ys, inv, gate, T, shared=1)
+    # sum_k g_k x = x (gates sum to one) up to K roundings
+    assert np.all(np.abs(y - x) <= (K + 1) * 2.0 ** -24 * np.abs(x) * 2 + 1e-30)
+
+
+def test_combine_dyadic_exact(orc):
+    rng = np.random.default_rng(11)
+    T, H, K = 7, 32, 4
+    R = T * K + T
+    ys = rng.integers(-64, 64, (R, H)).astype(F32)
+    inv = np.stack([rng.permutation(T * K)[:K] for _ in range(T)]).astype(np.int32)
+    gate = np.tile(np.array([0.5, 0.25, 0.125, 0.125], F32), (T, 1))
+    y = orc.combine(ys, inv, gate, T, shared=1)
+    ref = ys[T * K:].astype(np.float64) + sum(gate[:, k:k + 1].astype(np.float64) *
+                                               ys[inv[:, k]].astype(np.float64) for k in range(K))
+    assert np.array_equal(y.astype(np.float64), ref)
+
+
+def test_combine_order_is_rank_order_then_shared(orc):
+    # g*Y terms 2^24 and 1 and -2^24 in rank order: fma chain gives 0, then shared 1 -> 1.
+    ys = np.array([[2.0 ** 24], [1.0], [-2.0 ** 24], [1.0]], F32)
+    inv = np.array([[0, 1, 2]], np.int32)
+    gate = np.ones((1, 3), F32)
+    y = orc.combine(ys, inv, gate, 1, shared=1)
+    assert y[0, 0] == 1.0
+
+
+def test_combine_bf16_rounding(orc):
+    rng = np.random.default_rng(12)
+    T, H, K = 5, 64, 2
+    ysf = rng.standard_normal((T * K + T, H)).astype(F32)
+    ysb = torch.from_numpy(ysf).to(torch.bfloat16)
+    ysn = ysb.view(torch.int16).numpy().view(np.uint16)
+    inv = np.arange(T * K, dtype=np.int32).reshape(T, K)
+    gate = np.tile(np.array([0.75, 0.25], F32), (T, 1))
+    y = orc.combine(ysn, inv, gate, T, shared=1)
+    yf = ysb.float().numpy().astype(np.float64)
+    acc = yf[T * K:] + (0.75 * yf[inv[:, 0]] + 0.25 * yf[inv[:, 1]])  # exact in float64
+    ref = torch.from_numpy(acc.astype(F32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    # exact when the float32 accumulation was exact (true for most elements)
+    exact32 = acc == acc.astype(F32).astype(np.float64)
+    assert np.array_equal(y[exact32], ref[exact32])
+
+
+# --------------------------------------------------------------------------- bias update
+
+def test_bias_update_sign_rule(orc):
+    E, T, K = 8, 6, 4                      # mean load T*K/E = 3
+    counts = np.array([3, 4, 2, 0, 9, 3, 2, 1], np.int32)
+    assert counts.sum() == T * K
+    b = np.linspace(-0.02, 0.02, E).astype(F32)
+    nb = orc.bias_update(counts, T, K, 0.01, b)
+    g = F32(0.01)
+    for e in range(E):
+        if counts[e] * E > T * K:
+            assert nb[e] == F32(b[e] - g)
+        elif counts[e] * E < T * K:
+            assert nb[e] == F32(b[e] + g)
+        else:
+            assert nb[e] == b[e]
+
+
+def test_bias_update_fractional_mean_and_balanced(orc):
+    # T*K/E = 1.5: 1 is under (+gamma), 2 is over (-gamma)
+    nb = orc.bias_update(np.array([1, 2], np.int32), 3, 1, 0.01, np.zeros(2, F32))
+    assert nb.tolist() == [F32(0.01), F32(-0.01)]
+    b = np.array([0.3, -0.2, 0.0, 0.1], F32)
+    assert np.array_equal(orc.bias_update(np.array([5, 5, 5, 5], np.int32), 10, 2, 0.01, b), b)
+
+
+def test_pages_constants_fixture():
+    with open(os.path.join(GOLDEN, "pages_constants.json")) as f:
+        c = json.load(f)
+    import workloads
+    w = workloads.get("v3-bf16")
+    assert (w.E, w.S, w.K, w.H, w.M) == (c["routed_experts"], c["shared_experts"], c["top_k"],
+                                         c["hidden"], c["max_nodes_per_token"])
+    assert w.gamma == c["gamma_start"]
+    assert workloads.W_STD == c["init_std"]
+
+
+# --------------------------------------------------------------------------- whole layer
+
+def test_forward_f32_against_dense_float64(orc):
+    import workloads
+    w = workloads.get("tiny-fp32")
+    Wt = workloads.make_weights(w)
+    x = workloads.make_x(w).numpy()
+    wr, b = Wt["w_router"].numpy(), Wt["bias"].numpy()
+    w13, w2 = Wt["w13"].numpy(), Wt["w2"].numpy()
+    out = orc.forward(x, wr, b, w13, w2, w.G, w.M, w.K, w.J)
+    xd = x.astype(np.float64)
+
+    def ffn(e, rows):
+        h = swiglu_f64(rows, w13[e].astype(np.float64), None, w.I).astype(F32)
+        return h.astype(np.float64) @ w2[e].astype(np.float64).T
+
+    ref = ffn(w.E, xd)
+    for t in range(w.T):
+        for k in range(w.K):
+            ref[t] += out["topk_gate"][t, k] * ffn(out["topk_idx"][t, k], xd[t:t + 1])[0]
+    err = np.abs(out["y"] - ref).max() / np.abs(ref).max()
+    assert err < 1e-6, err
+
+
+def test_forward_threads_bitwise(orc):
+    import workloads
+    w = workloads.get("tiny-fp32", T=64)
+    Wt = workloads.make_weights(w)
+    x = workloads.make_x(w).numpy()
+    args = (x, Wt["w_router"].numpy(), Wt["bias"].numpy(), Wt["w13"].numpy(), Wt["w2"].numpy(),
+            w.G, w.M, w.K, w.J)
+    a = orc.forward(*args, nthreads=1)
+    b = orc.forward(*args, nthreads=8)
+    for k in ("topk_idx", "topk_gate", "y_sorted", "y"):
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8))
+
+
+def test_balancing_loop_reduces_imbalance(orc):
+    # The pages describe loads moving from disorder towards uniform under the bias rule.
+    rng = np.random.default_rng(13)
+    T, E, G, M, K = 512, 16, 4, 2, 4
+    offs = np.log(np.arange(1, E + 1, dtype=np.float64) ** -1.2)[rng.permutation(E)].astype(F32)
+    b = np.zeros(E, F32)
+    ratios = []
+    for step in range(60):
+        z = (rng.standard_normal((T, E)) * 0.3).astype(F32) + offs
+        idx, gate, counts = orc.select(z, b, G, M, K, 2)
+        ratios.append(counts.max() / (T * K / E))
+        b = orc.bias_update(counts, T, K, 0.01, b)
+    assert ratios[0] > 2.0
+    assert max(ratios[-10:]) < 0.75 * ratios[0]

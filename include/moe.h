@@ -1,0 +1,178 @@
+/*
+ * moe.h -- C ABI of libmoe, the MI355X (gfx950) DeepSeekMoE layer forward with
+ * auxiliary-loss-free load balancing.
+ *
+ * The layer (DeepSeek-V3 report, as summarised on mpbf.cn "DeepSeek-V3技术报告",
+ * section 2.2 "DeepSeekMoE 与无辅助损失"):
+ *   - the FFN is one always-on shared expert plus E fine-grained routed experts;
+ *   - token-expert affinity s = sigmoid(x . w_router[e]);
+ *   - each expert carries a bias b[e] that is added to s only to choose experts;
+ *   - the choice is limited to M of G expert groups (the single-GPU form of
+ *     node-limited routing: groups ranked by the summed affinity of their experts);
+ *   - the gate of a chosen expert is its unbiased s divided by the sum of s over the
+ *     K chosen experts;
+ *   - no token is dropped; per-expert loads over the whole batch drive the bias
+ *     update after each step: overloaded experts lose gamma, underloaded gain gamma.
+ * The output is the shared expert's output plus the gate-weighted routed outputs
+ * (blog.resmic.cn "DeepSeek-V3架构深度解析", section 核心架构二).
+ *
+ * One forward step is five calls on one stream:
+ *   moe_route -> moe_permute -> moe_expert_ffn -> moe_combine, then moe_bias_update.
+ *
+ * Conventions for every call
+ *   - All tensor pointers are DEVICE pointers, row-major, contiguous, 16-byte aligned.
+ *     The caller owns and allocates every buffer, including the workspace; the library
+ *     never allocates or frees device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls only
+ *     enqueue work; none synchronises the host.
+ *   - Arguments are validated before anything is launched.  On a negative status
+ *     nothing was enqueued and no output was written; moe_last_error() gives the reason
+ *     (a per-thread string).
+ *   - Outputs are overwritten entirely; the only in/out argument is `bias`.
+ *   - Calls that share no output buffers may run concurrently on different streams; the
+ *     library keeps no mutable global state apart from the per-thread error string.
+ *
+ * Problem limits (checked): 1 <= T, T*(K+1) < 2^31; H % 128 == 0, 128 <= H <= 65536;
+ * I % 128 == 0, 128 <= I <= 32768; 1 <= E <= 512, E % G == 0, 1 <= G <= 64,
+ * 1 <= M <= G, 1 <= J <= min(E/G, 8), 1 <= K <= min(M*E/G, 16); S in {0, 1}.
+ * Dtypes: act_dtype F32 with expert_dtype F32, or act_dtype BF16 with expert_dtype
+ * BF16 or FP8_E4M3.  Inputs must be finite.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* a size, pointer or dtype violates the limits above */
+  MOE_ERR_UNSUPPORTED = -2, /* no kernel for this combination (e.g. no gfx950 device) */
+  MOE_ERR_WORKSPACE = -3,   /* ws is NULL or smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+typedef struct moe_problem {
+  int64_t T;            /* tokens in the batch (one step)                              */
+  int32_t H;            /* hidden width                                                */
+  int32_t E;            /* routed experts                                              */
+  int32_t G;            /* expert groups (experts g*E/G .. (g+1)*E/G-1 form group g)    */
+  int32_t M;            /* groups a token may use                                      */
+  int32_t K;            /* routed experts per token                                    */
+  int32_t J;            /* keys summed into a group's score                            */
+  int32_t I;            /* FFN (SwiGLU) width of every expert                          */
+  int32_t S;            /* shared experts: 0 or 1                                      */
+  int32_t act_dtype;    /* moe_dtype of x, y_sorted and y: MOE_F32 | MOE_BF16           */
+  int32_t expert_dtype; /* moe_dtype of the GEMM operands: MOE_F32 | MOE_BF16 | FP8     */
+} moe_problem;
+
+/* Rows of the permuted buffers: R = T*K + S*T (routed rows, then T shared rows). */
+
+enum { MOE_CALL_ROUTE = 0, MOE_CALL_PERMUTE = 1, MOE_CALL_EXPERT_FFN = 2 };
+
+/* Workspace bytes a call needs for problem p (0 if none).  Returns 0 and sets the
+ * last error for an invalid problem or call id. */
+size_t moe_workspace_bytes(const moe_problem* p, int32_t which_call);
+
+/* Routing (mpbf.cn section 2.2; node-limited routing in the same section).
+ *   x         [T,H]  act_dtype   token activations
+ *   w_router  [E,H]  fp32        router weight
+ *   bias      [E]    fp32        per-expert routing bias
+ *   topk_idx  [T,K]  int32  out  chosen experts, in rank order (largest key first)
+ *   topk_gate [T,K]  fp32   out  s / sum of s over the K chosen (unbiased)
+ *   expert_counts [E] int32 out  tokens routed to each expert in this batch
+ *   logits_out [T,E] fp32   out  router logits z, or NULL to keep them in ws
+ *   ws        >= moe_workspace_bytes(p, MOE_CALL_ROUTE) bytes (T*E*4 when logits_out
+ *             is NULL; the same size is reported either way)
+ * Numerics: z[t,e] is a sequential fused multiply-add chain over h = 0..H-1 from +0;
+ * s = 1/(1+exp(-clamp(z,-80,80))) with a Cody-Waite/Taylor-7 exp; key = s + bias;
+ * group score = fp32 sum, from 0, of the group's J largest keys; groups and experts
+ * are ranked by (value descending, index ascending); gate = s / sum (IEEE division).
+ * The result is bit-for-bit reproducible. */
+moe_status moe_route(const moe_problem* p, const void* x, const float* w_router,
+                     const float* bias, int32_t* topk_idx, float* topk_gate,
+                     int32_t* expert_counts, float* logits_out, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Permute: the single-GPU form of the dispatch step (mpbf.cn section 3.2: a block is
+ * attention / dispatch / expert MLP / combine).  Rows are grouped by expert in index
+ * order; within an expert, tokens ascend; the shared expert (S = 1) is the last group
+ * and holds every token in order.
+ *   x            [T,H] act_dtype
+ *   topk_idx     [T,K] int32   from moe_route (values outside [0,E) are skipped and
+ *                              their inv_perm entry is -1; the layout is then undefined)
+ *   offsets      [E+S+1] int32 out  first row of each group; offsets[E] = T*K
+ *   sorted_token [R]     int32 out  token of each row
+ *   inv_perm     [T,K]   int32 out  row holding (t, topk_idx[t,k])
+ *   x_sorted     [R,H]   out  act_dtype rows, or FP8 E4M3 codes when expert_dtype is
+ *                             FP8 (each token quantised once per 128-column tile:
+ *                             scale = amax/448, code = RNE-saturating E4M3 of x/scale)
+ *   x_sorted_scale [R,H/128] fp32 out (FP8 only, else NULL)
+ *   ws           >= moe_workspace_bytes(p, MOE_CALL_PERMUTE) bytes
+ * Deterministic: every output is a pure function of the inputs. */
+moe_status moe_permute(const moe_problem* p, const void* x, const int32_t* topk_idx,
+                       int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm,
+                       void* x_sorted, float* x_sorted_scale, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Expert FFNs (SwiGLU) of every group as one grouped GEMM pair:
+ *   h = silu(x W13[g][0:I]^T) * (x W13[g][I:2I]^T),  Y = h W2[g]^T,
+ * fp32 accumulation (FP8: per-128-deep block partial sums scaled by the two block
+ * scales and accumulated in fp32 -- mpbf.cn section 3.1, tile-wise scaling and
+ * higher-precision accumulation; joto.ai item 3, FP8 inputs and weights, FP32
+ * accumulation).  h is stored at the activation precision (FP8: quantised per
+ * (row, 128 columns) like x); Y is rounded to act_dtype.
+ *   x_sorted, x_sorted_scale, offsets   from moe_permute
+ *   w13  [E+S, 2I, H]  expert_dtype (rows 0..I-1 gate, I..2I-1 up; shared expert last)
+ *   w13_scale [E+S, 2I/128, H/128] fp32 (FP8 only, else NULL)
+ *   w2   [E+S, H, I]   expert_dtype
+ *   w2_scale  [E+S, H/128, I/128]  fp32 (FP8 only, else NULL)
+ *   y_sorted  [R,H] act_dtype out
+ *   ws   >= moe_workspace_bytes(p, MOE_CALL_EXPERT_FFN) bytes (holds h and the tile
+ *        schedule)
+ * offsets must be the values moe_permute wrote (they are read on the device). */
+moe_status moe_expert_ffn(const moe_problem* p, const void* x_sorted,
+                          const float* x_sorted_scale, const int32_t* offsets,
+                          const void* w13, const float* w13_scale, const void* w2,
+                          const float* w2_scale, void* y_sorted, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Combine (blog.resmic.cn section 核心架构二: shared output + gate-weighted routed
+ * outputs):  acc = 0; for k = 0..K-1: acc = fma(gate[t,k], Y[inv_perm[t,k]], acc);
+ * if S: acc = Y[T*K + t] + acc;  y[t] = acc rounded (RNE) to act_dtype.
+ *   y_sorted [R,H] act_dtype, inv_perm [T,K] int32, topk_gate [T,K] fp32,
+ *   y [T,H] act_dtype out.  Bit-for-bit reproducible for given inputs. */
+moe_status moe_combine(const moe_problem* p, const void* y_sorted, const int32_t* inv_perm,
+                       const float* topk_gate, void* y, void* stream);
+
+/* Bias update after a step (mpbf.cn sections 2.2 and 6.2; joto.ai item 1):
+ * for each expert, compare its load with the uniform share exactly in integers,
+ *   counts[e]*E > T*K  ->  bias[e] -= gamma;   counts[e]*E < T*K  ->  bias[e] += gamma;
+ *   equal -> unchanged   (fp32 arithmetic; the bias never takes a gradient).
+ *   expert_counts [E] int32 (from moe_route), bias [E] fp32 in/out. */
+moe_status moe_bias_update(const moe_problem* p, const int32_t* expert_counts, float gamma,
+                           float* bias, void* stream);
+
+/* Offline FP8 preparation of expert weights (mpbf.cn section 4.3: block-wise scaling
+ * instead of one global scale): for `batch` bf16 matrices [rows, cols] (rows and cols
+ * multiples of 128) write E4M3 codes [batch, rows, cols] and fp32 scales
+ * [batch, rows/128, cols/128], one per 128x128 block: scale = amax/448 (1 if amax is 0),
+ * code = RNE-saturating E4M3 of w/scale. */
+moe_status moe_quantize_weights_fp8(const void* w_bf16, void* w_fp8, float* scale,
+                                    int64_t batch, int32_t rows, int32_t cols, void* stream);
+
+/* Text of a status code, and the last error message of the calling thread. */
+const char* moe_status_str(moe_status s);
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,139 @@
+"""Thin ctypes binding of libmoe.so: the C ABI's calls under the same names.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels behind
+these calls.  Tensors are passed as device pointers (``tensor.data_ptr()``) with the
+current torch stream.  There is no fallback: if the library is missing or the
+device is not gfx950 the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_EXPERT_FFN = 0, 1, 2
+
+EXPORTS = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_bias_update",
+           "moe_quantize_weights_fp8", "moe_workspace_bytes", "moe_status_str", "moe_last_error")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, call: str, msg: str):
+        super().__init__(f"{call} failed with status {status}: {msg}")
+        self.status = status
+
+
+class moe_problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("G", ctypes.c_int32), ("M", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("J", ctypes.c_int32), ("I", ctypes.c_int32), ("S", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mixture_experts_layer_added_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32, i64, f32 = (ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64,
+                                 ctypes.c_float)
+        pp = ctypes.POINTER(moe_problem)
+        L.moe_route.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_permute.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_expert_ffn.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_combine.argtypes = [pp, vp, vp, vp, vp, vp]
+        L.moe_bias_update.argtypes = [pp, vp, f32, vp, vp]
+        L.moe_quantize_weights_fp8.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+        L.moe_workspace_bytes.argtypes = [pp, i32]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_status_str.argtypes = [i32]
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        for n in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_bias_update",
+                  "moe_quantize_weights_fp8"):
+            getattr(L, n).restype = i32
+        _lib = L
+    return _lib
+
+
+def problem(T, H, E, G, M, K, J, I, S=1, act_dtype=MOE_BF16, expert_dtype=MOE_BF16) -> moe_problem:
+    return moe_problem(T, H, E, G, M, K, J, I, S, act_dtype, expert_dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, call: str):
+    if status != MOE_OK:
+        raise MoeError(status, call, lib().moe_last_error().decode())
+
+
+def last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def moe_workspace_bytes(p: moe_problem, which_call: int) -> int:
+    return lib().moe_workspace_bytes(ctypes.byref(p), which_call)
+
+
+def moe_route(p, x, w_router, bias, topk_idx, topk_gate, expert_counts, logits_out=None,
+              ws=None, ws_bytes=0, stream=None):
+    _check(lib().moe_route(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(topk_idx),
+                           _ptr(topk_gate), _ptr(expert_counts), _ptr(logits_out), _ptr(ws),
+                           ws_bytes, _stream(stream)), "moe_route")
+
+
+def moe_permute(p, x, topk_idx, offsets, sorted_token, inv_perm, x_sorted, x_sorted_scale=None,
+                ws=None, ws_bytes=0, stream=None):
+    _check(lib().moe_permute(ctypes.byref(p), _ptr(x), _ptr(topk_idx), _ptr(offsets),
+                             _ptr(sorted_token), _ptr(inv_perm), _ptr(x_sorted),
+                             _ptr(x_sorted_scale), _ptr(ws), ws_bytes, _stream(stream)),
+           "moe_permute")
+
+
+def moe_expert_ffn(p, x_sorted, x_sorted_scale, offsets, w13, w13_scale, w2, w2_scale, y_sorted,
+                   ws=None, ws_bytes=0, stream=None):
+    _check(lib().moe_expert_ffn(ctypes.byref(p), _ptr(x_sorted), _ptr(x_sorted_scale),
+                                _ptr(offsets), _ptr(w13), _ptr(w13_scale), _ptr(w2),
+                                _ptr(w2_scale), _ptr(y_sorted), _ptr(ws), ws_bytes,
+                                _stream(stream)), "moe_expert_ffn")
+
+
+def moe_combine(p, y_sorted, inv_perm, topk_gate, y, stream=None):
+    _check(lib().moe_combine(ctypes.byref(p), _ptr(y_sorted), _ptr(inv_perm), _ptr(topk_gate),
+                             _ptr(y), _stream(stream)), "moe_combine")
+
+
+def moe_bias_update(p, expert_counts, gamma, bias, stream=None):
+    _check(lib().moe_bias_update(ctypes.byref(p), _ptr(expert_counts), float(gamma), _ptr(bias),
+                                 _stream(stream)), "moe_bias_update")
+
+
+def moe_quantize_weights_fp8(w_bf16, w_fp8, scale, batch, rows, cols, stream=None):
+    _check(lib().moe_quantize_weights_fp8(_ptr(w_bf16), _ptr(w_fp8), _ptr(scale), batch, rows,
+                                          cols, _stream(stream)), "moe_quantize_weights_fp8")

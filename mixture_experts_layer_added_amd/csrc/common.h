@@ -1,0 +1,83 @@
+// Internal declarations shared by the HIP kernels and the C ABI of libmoe.
+// gfx950 only: wave64, MFMA, 160 KB LDS per CU, 8 XCDs of 32 CUs.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (inputs are finite on every path here).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// E4M3 (OCP) code of v with round-to-nearest-even and saturation at +-448: the
+// hardware conversion rounds to nearest even but maps |v| >= 464 to NaN, so the
+// input is clamped first.
+__device__ __forceinline__ uint32_t f32_to_e4m3_bits(float v) {
+  v = __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false)) & 0xFFu;
+}
+
+// Pack four E4M3 codes (little-endian byte order) from four floats.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
+  b = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
+  c = __builtin_fminf(__builtin_fmaxf(c, -448.0f), 448.0f);
+  d = __builtin_fminf(__builtin_fmaxf(d, -448.0f), 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// ---- launchers (each returns hipGetLastError() of its launch) ----
+struct Dims {
+  int64_t T;
+  int H, E, G, M, K, J, I, S;
+  int act, expert;  // moe_dtype codes
+  int64_t R() const { return T * K + (S ? T : 0); }
+};
+
+hipError_t launch_route(const Dims& d, const void* x, const float* w_router, const float* bias,
+                        int32_t* idx, float* gate, int32_t* counts, float* logits,
+                        hipStream_t st);
+
+size_t permute_ws_bytes(const Dims& d);
+hipError_t launch_permute(const Dims& d, const void* x, const int32_t* idx, int32_t* offsets,
+                          int32_t* sorted_token, int32_t* inv_perm, void* x_sorted,
+                          float* x_scale, void* ws, hipStream_t st);
+
+size_t ffn_ws_bytes(const Dims& d);
+hipError_t launch_expert_ffn(const Dims& d, const void* xs, const float* xs_scale,
+                             const int32_t* offsets, const void* w13, const float* w13_scale,
+                             const void* w2, const float* w2_scale, void* ys, void* ws,
+                             hipStream_t st);
+
+hipError_t launch_combine(const Dims& d, const void* ys, const int32_t* inv_perm,
+                          const float* gate, void* y, hipStream_t st);
+
+hipError_t launch_bias_update(const Dims& d, const int32_t* counts, float gamma, float* bias,
+                              hipStream_t st);
+
+hipError_t launch_quantize_weights(const uint16_t* w, uint8_t* q, float* scale, int64_t batch,
+                                   int rows, int cols, hipStream_t st);
+
+int device_cu_count();
+
+}  // namespace moe

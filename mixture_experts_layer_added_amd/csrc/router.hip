@@ -1,0 +1,298 @@
+// Router: logits, sigmoid affinities, bias-steered group-limited top-K, gates and
+// per-expert counts (DeepSeek-V3 report summary on mpbf.cn, section 2.2: sigmoid
+// gating renormalised over the chosen experts; a per-expert bias that only steers
+// the choice; node-limited routing by the summed affinity of each node's experts;
+// whole-batch expert loads).
+//
+// Numerics are fixed so the result is reproducible bit for bit:
+//   z[t,e]  = sequential fused multiply-add over h = 0..H-1, starting from +0
+//             (fp32 VALU, compiled without contraction; MFMA is not used because
+//             its internal summation order is not a sequential chain)
+//   s       = 1 / (1 + exp(-clamp(z, -80, 80)))   with exp by Cody-Waite
+//             reduction and a degree-7 Taylor polynomial (Horner, fused)
+//   key     = s + bias[e]
+//   group   = fp32 sum from 0 of the J largest keys of the group
+//   ranking = (value descending, index ascending) for groups and experts
+//   gate    = s / (s_0 + s_1 + ... + s_{K-1}) in rank order, IEEE division
+#include "common.h"
+
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Logits: a 64-token x 64-expert tile per 256-thread workgroup, each thread a
+// 4x4 register tile.  Hidden chunks of 32 go through LDS transposed ([h][token]
+// and [h][expert]) so one 16-byte LDS read gives a thread its 4 tokens (or 4
+// experts) at one h; every accumulator sees h in increasing order.
+// ---------------------------------------------------------------------------
+constexpr int LT = 64, LE = 64, LH = 32;
+
+template <typename XT>
+__global__ __launch_bounds__(256) void k_router_logits(const XT* __restrict__ x,
+                                                       const float* __restrict__ w, float* __restrict__ z,
+                                                       int32_t* __restrict__ counts, int T, int H, int E) {
+  __shared__ __attribute__((aligned(16))) float xs[2][LH][LT];
+  __shared__ __attribute__((aligned(16))) float wsm[2][LH][LE];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * LT, e0 = blockIdx.y * LE;
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int e = tid; e < E; e += 256) counts[e] = 0;  // zeroed before the select kernel runs
+
+  // loader mapping: 4 threads per row, 8 consecutive h each
+  const int lrow = tid >> 2, lh = (tid & 3) * 8;
+  const int xt = min(t0 + lrow, T - 1);
+  const int we = min(e0 + lrow, E - 1);
+  const XT* xp = x + (int64_t)xt * H + lh;
+  const float* wp = w + (int64_t)we * H + lh;
+
+  float xr[8], wr[8];
+  auto gload = [&](int h0) {
+    if constexpr (sizeof(XT) == 2) {
+      uint4 v = *reinterpret_cast<const uint4*>(xp + h0);
+      uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xr[2 * i] = __uint_as_float(u[i] << 16);
+        xr[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+      }
+    } else {
+      float4 a = *reinterpret_cast<const float4*>(xp + h0);
+      float4 b = *reinterpret_cast<const float4*>(xp + h0 + 4);
+      xr[0] = a.x; xr[1] = a.y; xr[2] = a.z; xr[3] = a.w;
+      xr[4] = b.x; xr[5] = b.y; xr[6] = b.z; xr[7] = b.w;
+    }
+    float4 a = *reinterpret_cast<const float4*>(wp + h0);
+    float4 b = *reinterpret_cast<const float4*>(wp + h0 + 4);
+    wr[0] = a.x; wr[1] = a.y; wr[2] = a.z; wr[3] = a.w;
+    wr[4] = b.x; wr[5] = b.y; wr[6] = b.z; wr[7] = b.w;
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      xs[buf][lh + i][lrow] = xr[i];
+      wsm[buf][lh + i][lrow] = wr[i];
+    }
+  };
+
+  const int ty = tid >> 4, tx = tid & 15;  // tokens ty*4.., experts tx*4..
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+
+  const int nchunk = H / LH;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nchunk) gload((c + 1) * LH);
+#pragma unroll 8
+    for (int hh = 0; hh < LH; ++hh) {
+      const float4 xv = *reinterpret_cast<const float4*>(&xs[buf][hh][ty * 4]);
+      const float4 wv = *reinterpret_cast<const float4*>(&wsm[buf][hh][tx * 4]);
+      const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
+      const float wa[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(xa[i], wa[j], acc[i][j]);
+    }
+    if (c + 1 < nchunk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + ty * 4 + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tx * 4 + j;
+      if (e < E) z[(int64_t)t * E + e] = acc[i][j];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// exp and sigmoid.  ln 2 is split for Cody-Waite reduction: the high part is ln 2
+// rounded to 16 significant bits (45426/65536) so k*LN2_HI is exact for |k| < 256;
+// the low part is the float nearest ln 2 - LN2_HI.  The polynomial is the Taylor
+// series of exp to degree 7 with coefficients rounded to float (1/n!).  |a| <= 80
+// keeps k within [-116, 116] and 2^k a normal float, so the final scaling is exact.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float exp_cw7(float a) {
+  constexpr float kInvLn2 = 0x1.715476p+0f;
+  constexpr float kLn2Hi = 0x1.62e4p-1f;
+  constexpr float kLn2Lo = 0x1.7f7d1cp-20f;
+  const float k = __builtin_rintf(a * kInvLn2);
+  float r = __builtin_fmaf(-k, kLn2Hi, a);
+  r = __builtin_fmaf(-k, kLn2Lo, r);
+  float p = 0x1.a01a02p-13f;
+  p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);
+  p = __builtin_fmaf(p, r, 0x1.111112p-7f);
+  p = __builtin_fmaf(p, r, 0x1.555556p-5f);
+  p = __builtin_fmaf(p, r, 0x1.555556p-3f);
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  return p * __uint_as_float(static_cast<uint32_t>(static_cast<int>(k) + 127) << 23);
+}
+
+__device__ __forceinline__ float affinity(float z) {
+  const float zc = __builtin_fminf(__builtin_fmaxf(z, -80.0f), 80.0f);
+  return 1.0f / (1.0f + exp_cw7(-zc));
+}
+
+// (value, index) ordering: larger value first, then the lower index.
+__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// ---------------------------------------------------------------------------
+// Selection: one wave per token, 4 tokens per workgroup.  Lane l holds experts
+// l, l+64, ... (at most 8).  Keys and affinities go to LDS; lane g < G ranks the
+// keys of group g and sums its J best; lane g then ranks its group among all G;
+// K rounds of a wave-wide (key, index) argmax over the kept groups pick the experts
+// in rank order.
+// ---------------------------------------------------------------------------
+constexpr int kMaxE = 512, kMaxPer = kMaxE / kWave, kMaxJ = 8, kMaxG = 64;
+
+__global__ __launch_bounds__(256) void k_router_select(const float* __restrict__ z,
+                                                       const float* __restrict__ bias,
+                                                       int32_t* __restrict__ idx, float* __restrict__ gate,
+                                                       int32_t* __restrict__ counts, int T, int E, int G,
+                                                       int M, int K, int J) {
+  __shared__ float s_key[4][kMaxE];
+  __shared__ float s_aff[4][kMaxE];
+  __shared__ float s_gscore[4][kMaxG];
+  __shared__ int s_kept[4][kMaxG];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t_raw = blockIdx.x * 4 + wv;
+  const bool live = t_raw < T;
+  const int t = live ? t_raw : T - 1;
+  const int gs = E / G;
+  const int per = (E + kWave - 1) / kWave;
+
+  float key[kMaxPer];
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    key[i] = 0.0f;
+    const int e = lane + kWave * i;
+    if (i < per && e < E) {
+      const float s = affinity(z[(int64_t)t * E + e]);
+      key[i] = s + bias[e];
+      s_key[wv][e] = key[i];
+      s_aff[wv][e] = s;
+    }
+  }
+  __syncthreads();
+
+  if (lane < G) {
+    // ordered list of the best keys so far, kept by carrying each new key down the
+    // list and swapping where it ranks first (static indices: stays in registers)
+    float top[kMaxJ];
+    int topi[kMaxJ];
+#pragma unroll
+    for (int q = 0; q < kMaxJ; ++q) {
+      top[q] = -__builtin_inff();
+      topi[q] = 0x7FFFFFFF;
+    }
+    for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
+      float v = s_key[wv][e];
+      int vi = e;
+#pragma unroll
+      for (int q = 0; q < kMaxJ; ++q) {
+        if (ranks_before(v, vi, top[q], topi[q])) {
+          const float tv = top[q];
+          const int ti = topi[q];
+          top[q] = v;
+          topi[q] = vi;
+          v = tv;
+          vi = ti;
+        }
+      }
+    }
+    float sc = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kMaxJ; ++q)
+      if (q < J) sc = sc + top[q];
+    s_gscore[wv][lane] = sc;
+  }
+  __syncthreads();
+  if (lane < G) {
+    const float mine = s_gscore[wv][lane];
+    int rank = 0;
+    for (int g = 0; g < G; ++g)
+      rank += ranks_before(s_gscore[wv][g], g, mine, lane) ? 1 : 0;
+    s_kept[wv][lane] = rank < M;
+  }
+  __syncthreads();
+
+  bool avail[kMaxPer];
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    const int e = lane + kWave * i;
+    avail[i] = (i < per) && (e < E) && s_kept[wv][e / gs];
+  }
+  int my_e = 0;
+  float my_s = 0.0f;
+  for (int r = 0; r < K; ++r) {
+    float bv = -__builtin_inff();
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      const int e = lane + kWave * i;
+      if (avail[i] && ranks_before(key[i], e, bv, bi)) {
+        bv = key[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ranks_before(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (bi >= E) bi = 0;  // unreachable: K <= M*E/G candidates always exist
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i)
+      if (bi == lane + kWave * i) avail[i] = false;
+    if (lane == r) {
+      my_e = bi;
+      my_s = s_aff[wv][bi];
+    }
+  }
+  float sum = 0.0f;
+  for (int r = 0; r < K; ++r) sum = sum + __shfl(my_s, r);
+  if (live && lane < K) {
+    idx[(int64_t)t * K + lane] = my_e;
+    gate[(int64_t)t * K + lane] = my_s / sum;
+    atomicAdd(&counts[my_e], 1);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route(const Dims& d, const void* x, const float* w_router, const float* bias,
+                        int32_t* idx, float* gate, int32_t* counts, float* logits,
+                        hipStream_t st) {
+  const int T = static_cast<int>(d.T);
+  dim3 g1((T + LT - 1) / LT, (d.E + LE - 1) / LE);
+  if (d.act == MOE_BF16)
+    hipLaunchKernelGGL(k_router_logits<uint16_t>, g1, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(x), w_router, logits, counts, T, d.H, d.E);
+  else
+    hipLaunchKernelGGL(k_router_logits<float>, g1, dim3(256), 0, st,
+                       static_cast<const float*>(x), w_router, logits, counts, T, d.H, d.E);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_router_select, dim3((T + 3) / 4), dim3(256), 0, st, logits, bias, idx,
+                     gate, counts, T, d.E, d.G, d.M, d.K, d.J);
+  return hipGetLastError();
+}
+
+}  // namespace moe

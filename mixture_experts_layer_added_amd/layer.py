@@ -1,0 +1,127 @@
+"""MoE layer object: owns the device buffers of one batch size and issues the five
+C-ABI calls on the current stream.  Plumbing only (allocation and argument
+marshalling); every step runs in libmoe's HIP kernels.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib as L
+
+_DT = {"f32": L.MOE_F32, "bf16": L.MOE_BF16, "e4m3": L.MOE_FP8_E4M3}
+
+
+@dataclass
+class Shape:
+    T: int
+    H: int
+    E: int
+    G: int
+    M: int
+    K: int
+    J: int
+    I: int
+    S: int = 1
+    act: str = "bf16"
+    expert: str = "bf16"
+
+    def problem(self) -> L.moe_problem:
+        return L.problem(self.T, self.H, self.E, self.G, self.M, self.K, self.J, self.I, self.S,
+                         _DT[self.act], _DT[self.expert])
+
+    @property
+    def R(self) -> int:
+        return self.T * self.K + self.S * self.T
+
+
+def quantize_weights_fp8(w: torch.Tensor, stream=None):
+    """bf16 [batch, rows, cols] -> (E4M3 codes uint8 [batch, rows, cols],
+    fp32 scales [batch, rows/128, cols/128])."""
+    assert w.dtype == torch.bfloat16 and w.dim() == 3 and w.is_contiguous()
+    b, r, c = w.shape
+    q = torch.empty((b, r, c), dtype=torch.uint8, device=w.device)
+    s = torch.empty((b, r // 128, c // 128), dtype=torch.float32, device=w.device)
+    L.moe_quantize_weights_fp8(w, q, s, b, r, c, stream)
+    return q, s
+
+
+class MoELayer:
+    """Buffers for one batch of T tokens.
+
+    Weights: w_router [E,H] fp32, bias [E] fp32 (updated in place by bias_step),
+    w13 [E+S,2I,H] and w2 [E+S,H,I] in the expert dtype (uint8 E4M3 codes with
+    w13_scale / w2_scale for the FP8 path).
+    """
+
+    def __init__(self, shape: Shape, w_router, bias, w13, w2, w13_scale=None, w2_scale=None,
+                 device="cuda"):
+        self.shape = shape
+        self.p = shape.problem()
+        self.w_router, self.bias = w_router, bias
+        self.w13, self.w2, self.w13_scale, self.w2_scale = w13, w2, w13_scale, w2_scale
+        T, H, E, K, R = shape.T, shape.H, shape.E, shape.K, shape.R
+        act = torch.float32 if shape.act == "f32" else torch.bfloat16
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.topk_idx = torch.empty((T, K), **i32)
+        self.topk_gate = torch.empty((T, K), dtype=torch.float32, device=dev)
+        self.counts = torch.empty((E,), **i32)
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        self.offsets = torch.empty((E + shape.S + 1,), **i32)
+        self.sorted_token = torch.empty((R,), **i32)
+        self.inv_perm = torch.empty((T, K), **i32)
+        if shape.expert == "e4m3":
+            self.x_sorted = torch.empty((R, H), dtype=torch.uint8, device=dev)
+            self.x_scale = torch.empty((R, H // 128), dtype=torch.float32, device=dev)
+        else:
+            self.x_sorted = torch.empty((R, H), dtype=act, device=dev)
+            self.x_scale = None
+        self.y_sorted = torch.empty((R, H), dtype=act, device=dev)
+        self.y = torch.empty((T, H), dtype=act, device=dev)
+        self.ws = {}
+        for call in (L.MOE_CALL_ROUTE, L.MOE_CALL_PERMUTE, L.MOE_CALL_EXPERT_FFN):
+            n = L.moe_workspace_bytes(self.p, call)
+            if n == 0 and call != L.MOE_CALL_ROUTE:
+                raise L.MoeError(L.MOE_ERR_INVALID_ARG, "moe_workspace_bytes", L.last_error())
+            self.ws[call] = torch.empty((max(n, 256),), dtype=torch.uint8, device=dev)
+
+    def _ws(self, call):
+        t = self.ws[call]
+        return t, t.numel()
+
+    def route(self, x, stream=None):
+        L.moe_route(self.p, x, self.w_router, self.bias, self.topk_idx, self.topk_gate,
+                    self.counts, self.logits, None, 0, stream)
+
+    def permute(self, x, stream=None):
+        ws, n = self._ws(L.MOE_CALL_PERMUTE)
+        L.moe_permute(self.p, x, self.topk_idx, self.offsets, self.sorted_token, self.inv_perm,
+                      self.x_sorted, self.x_scale, ws, n, stream)
+
+    def expert_ffn(self, stream=None):
+        ws, n = self._ws(L.MOE_CALL_EXPERT_FFN)
+        L.moe_expert_ffn(self.p, self.x_sorted, self.x_scale, self.offsets, self.w13,
+                         self.w13_scale, self.w2, self.w2_scale, self.y_sorted, ws, n, stream)
+
+    def combine(self, stream=None):
+        L.moe_combine(self.p, self.y_sorted, self.inv_perm, self.topk_gate, self.y, stream)
+
+    def forward(self, x, stream=None):
+        """route -> permute -> expert FFN -> combine; returns self.y (overwritten by the
+        next call)."""
+        self.route(x, stream)
+        self.permute(x, stream)
+        self.expert_ffn(stream)
+        self.combine(stream)
+        return self.y
+
+    def bias_step(self, gamma=0.01, stream=None):
+        """Aux-loss-free bias update from this batch's expert counts (in place)."""
+        L.moe_bias_update(self.p, self.counts, gamma, self.bias, stream)
+
+    def step(self, x, gamma=0.01, stream=None):
+        y = self.forward(x, stream)
+        self.bias_step(gamma, stream)
+        return y

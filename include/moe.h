@@ -134,14 +134,33 @@ moe_status moe_permute(const moe_problem* p, const void* x, const int32_t* topk_
  *   w2   [E+S, H, I]   expert_dtype
  *   w2_scale  [E+S, H/128, I/128]  fp32 (FP8 only, else NULL)
  *   y_sorted  [R,H] act_dtype out
- *   ws   >= moe_workspace_bytes(p, MOE_CALL_EXPERT_FFN) bytes (holds h and the tile
- *        schedule)
- * offsets must be the values moe_permute wrote (they are read on the device). */
+ *   ws   >= moe_workspace_bytes(p, MOE_CALL_EXPERT_FFN) bytes (holds h: [R,I] of the
+ *        activation dtype, or [R,I] E4M3 codes followed by [R,I/128] fp32 scales for
+ *        FP8, the scales starting at the next 256-byte boundary)
+ * offsets must be the values moe_permute wrote (they are read on the device).
+ * Equivalent to moe_expert_ffn_up followed by moe_expert_ffn_down on ws. */
 moe_status moe_expert_ffn(const moe_problem* p, const void* x_sorted,
                           const float* x_sorted_scale, const int32_t* offsets,
                           const void* w13, const float* w13_scale, const void* w2,
                           const float* w2_scale, void* y_sorted, void* ws, size_t ws_bytes,
                           void* stream);
+
+/* First half of moe_expert_ffn (same passages): the gate/up grouped GEMM with SwiGLU.
+ *   h       [R,I] out: act_dtype, or E4M3 codes for FP8 (scale = amax/448 per
+ *           (row, 128 columns), code = RNE-saturating E4M3 of h/scale)
+ *   h_scale [R,I/128] fp32 out (FP8 only, else NULL)
+ * Other arguments as moe_expert_ffn.  Rows of h outside every group are not written. */
+moe_status moe_expert_ffn_up(const moe_problem* p, const void* x_sorted,
+                             const float* x_sorted_scale, const int32_t* offsets,
+                             const void* w13, const float* w13_scale, void* h, float* h_scale,
+                             void* stream);
+
+/* Second half of moe_expert_ffn: Y = h W2[g]^T per group, rounded to act_dtype.
+ *   h, h_scale from moe_expert_ffn_up; w2, w2_scale, offsets as moe_expert_ffn;
+ *   y_sorted [R,H] act_dtype out. */
+moe_status moe_expert_ffn_down(const moe_problem* p, const void* h, const float* h_scale,
+                               const int32_t* offsets, const void* w2, const float* w2_scale,
+                               void* y_sorted, void* stream);
 
 /* Combine (blog.resmic.cn section 核心架构二: shared output + gate-weighted routed
  * outputs):  acc = 0; for k = 0..K-1: acc = fma(gate[t,k], Y[inv_perm[t,k]], acc);

@@ -17,8 +17,9 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_EXPERT_FFN = 0, 1, 2
 
-EXPORTS = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_bias_update",
-           "moe_quantize_weights_fp8", "moe_workspace_bytes", "moe_status_str", "moe_last_error")
+EXPORTS = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_up",
+           "moe_expert_ffn_down", "moe_combine", "moe_bias_update", "moe_quantize_weights_fp8",
+           "moe_workspace_bytes", "moe_status_str", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -51,6 +52,8 @@ def lib():
         L.moe_route.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_permute.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_expert_ffn.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_expert_ffn_up.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_expert_ffn_down.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_combine.argtypes = [pp, vp, vp, vp, vp, vp]
         L.moe_bias_update.argtypes = [pp, vp, f32, vp, vp]
         L.moe_quantize_weights_fp8.argtypes = [vp, vp, vp, i64, i32, i32, vp]
@@ -60,7 +63,8 @@ def lib():
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
-        for n in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_bias_update",
+        for n in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_up",
+                  "moe_expert_ffn_down", "moe_combine", "moe_bias_update",
                   "moe_quantize_weights_fp8"):
             getattr(L, n).restype = i32
         _lib = L
@@ -122,6 +126,19 @@ def moe_expert_ffn(p, x_sorted, x_sorted_scale, offsets, w13, w13_scale, w2, w2_
                                 _ptr(offsets), _ptr(w13), _ptr(w13_scale), _ptr(w2),
                                 _ptr(w2_scale), _ptr(y_sorted), _ptr(ws), ws_bytes,
                                 _stream(stream)), "moe_expert_ffn")
+
+
+def moe_expert_ffn_up(p, x_sorted, x_sorted_scale, offsets, w13, w13_scale, h, h_scale=None,
+                      stream=None):
+    _check(lib().moe_expert_ffn_up(ctypes.byref(p), _ptr(x_sorted), _ptr(x_sorted_scale),
+                                   _ptr(offsets), _ptr(w13), _ptr(w13_scale), _ptr(h),
+                                   _ptr(h_scale), _stream(stream)), "moe_expert_ffn_up")
+
+
+def moe_expert_ffn_down(p, h, h_scale, offsets, w2, w2_scale, y_sorted, stream=None):
+    _check(lib().moe_expert_ffn_down(ctypes.byref(p), _ptr(h), _ptr(h_scale), _ptr(offsets),
+                                     _ptr(w2), _ptr(w2_scale), _ptr(y_sorted), _stream(stream)),
+           "moe_expert_ffn_down")
 
 
 def moe_combine(p, y_sorted, inv_perm, topk_gate, y, stream=None):

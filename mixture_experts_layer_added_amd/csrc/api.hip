@@ -174,6 +174,47 @@ moe_status moe_permute(const moe_problem* p, const void* x, const int32_t* topk_
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_permute launch");
 }
 
+moe_status moe_expert_ffn_up(const moe_problem* p, const void* x_sorted,
+                             const float* x_sorted_scale, const int32_t* offsets,
+                             const void* w13, const float* w13_scale, void* h, float* h_scale,
+                             void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  REQUIRE_PTR(x_sorted);
+  REQUIRE_PTR(w13);
+  REQUIRE_PTR(h);
+  if (!offsets) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL");
+  if (d.expert == MOE_FP8_E4M3 && (!x_sorted_scale || !w13_scale || !h_scale))
+    return fail(MOE_ERR_INVALID_ARG, "the FP8 path needs x_sorted_scale, w13_scale, h_scale");
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  hipError_t e = launch_ffn_up(d, x_sorted, x_sorted_scale, offsets, w13, w13_scale, h, h_scale,
+                               static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported)
+    return fail(MOE_ERR_UNSUPPORTED, "no expert FFN kernel for expert dtype %d", d.expert);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn_up launch");
+}
+
+moe_status moe_expert_ffn_down(const moe_problem* p, const void* h, const float* h_scale,
+                               const int32_t* offsets, const void* w2, const float* w2_scale,
+                               void* y_sorted, void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  REQUIRE_PTR(h);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(y_sorted);
+  if (!offsets) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL");
+  if (d.expert == MOE_FP8_E4M3 && (!h_scale || !w2_scale))
+    return fail(MOE_ERR_INVALID_ARG, "the FP8 path needs h_scale and w2_scale");
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  hipError_t e = launch_ffn_down(d, h, h_scale, offsets, w2, w2_scale, y_sorted,
+                                 static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported)
+    return fail(MOE_ERR_UNSUPPORTED, "no expert FFN kernel for expert dtype %d", d.expert);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn_down launch");
+}
+
 moe_status moe_expert_ffn(const moe_problem* p, const void* x_sorted,
                           const float* x_sorted_scale, const int32_t* offsets,
                           const void* w13, const float* w13_scale, const void* w2,
@@ -192,12 +233,10 @@ moe_status moe_expert_ffn(const moe_problem* p, const void* x_sorted,
   if (!ws || ws_bytes < ffn_ws_bytes(d) || !aligned16(ws))
     return fail(MOE_ERR_WORKSPACE, "expert_ffn needs %zu aligned workspace bytes, got %zu",
                 ffn_ws_bytes(d), ws ? ws_bytes : (size_t)0);
-  if ((s = check_device(nullptr)) != MOE_OK) return s;
-  hipError_t e = launch_expert_ffn(d, x_sorted, x_sorted_scale, offsets, w13, w13_scale, w2,
-                                   w2_scale, y_sorted, ws, static_cast<hipStream_t>(stream));
-  if (e == hipErrorNotSupported)
-    return fail(MOE_ERR_UNSUPPORTED, "no expert FFN kernel for expert dtype %d", d.expert);
-  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn launch");
+  float* h_scale = d.expert == MOE_FP8_E4M3 ? ffn_ws_h_scale(d, ws) : nullptr;
+  s = moe_expert_ffn_up(p, x_sorted, x_sorted_scale, offsets, w13, w13_scale, ws, h_scale, stream);
+  if (s != MOE_OK) return s;
+  return moe_expert_ffn_down(p, ws, h_scale, offsets, w2, w2_scale, y_sorted, stream);
 }
 
 moe_status moe_combine(const moe_problem* p, const void* y_sorted, const int32_t* inv_perm,

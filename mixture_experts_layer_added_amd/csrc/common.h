@@ -64,10 +64,19 @@ hipError_t launch_permute(const Dims& d, const void* x, const int32_t* idx, int3
                           float* x_scale, void* ws, hipStream_t st);
 
 size_t ffn_ws_bytes(const Dims& d);
-hipError_t launch_expert_ffn(const Dims& d, const void* xs, const float* xs_scale,
-                             const int32_t* offsets, const void* w13, const float* w13_scale,
-                             const void* w2, const float* w2_scale, void* ys, void* ws,
-                             hipStream_t st);
+float* ffn_ws_h_scale(const Dims& d, void* ws);
+hipError_t launch_ffn_up(const Dims& d, const void* xs, const float* xs_scale,
+                         const int32_t* offsets, const void* w13, const float* w13_scale, void* h,
+                         float* h_scale, hipStream_t st);
+hipError_t launch_ffn_down(const Dims& d, const void* h, const float* h_scale,
+                           const int32_t* offsets, const void* w2, const float* w2_scale, void* ys,
+                           hipStream_t st);
+hipError_t launch_fp8_up(const Dims& d, const void* xs, const float* xs_scale,
+                         const int32_t* offsets, const void* w13, const float* w13_scale, void* h,
+                         float* h_scale, hipStream_t st);
+hipError_t launch_fp8_down(const Dims& d, const void* h, const float* h_scale,
+                           const int32_t* offsets, const void* w2, const float* w2_scale, void* ys,
+                           hipStream_t st);
 
 hipError_t launch_combine(const Dims& d, const void* ys, const int32_t* inv_perm,
                           const float* gate, void* y, hipStream_t st);

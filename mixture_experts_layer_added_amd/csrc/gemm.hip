@@ -18,22 +18,38 @@ namespace moe {
 namespace {
 
 constexpr int kMaxGroups = 513;
+constexpr int kSchedPer = 9;  // groups per lane of wave 0 (64 * 9 >= kMaxGroups)
 
-__global__ __launch_bounds__(1024) void k_ffn_schedule(const int32_t* __restrict__ offsets,
-                                                       int32_t* __restrict__ mt_start, int NG,
-                                                       int BM) {
-  __shared__ int v[1024];
-  const int g = threadIdx.x;
-  v[g] = (g < NG) ? (offsets[g + 1] - offsets[g] + BM - 1) / BM : 0;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {
-    const int a = (g >= d) ? v[g - d] : 0;
-    __syncthreads();
-    v[g] += a;
-    __syncthreads();
+// Row-tile prefix sums of the groups into LDS: s_mt[g] = sum_{g' < g} ceil(m_g'/BM),
+// s_mt[NG] = total.  Wave 0 scans; the whole workgroup waits.
+__device__ __forceinline__ void build_schedule(const int32_t* __restrict__ offsets, int NG, int BM,
+                                               int* s_mt) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    int loc[kSchedPer];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < kSchedPer; ++i) {
+      const int g = lane * kSchedPer + i;
+      loc[i] = (g < NG) ? (offsets[g + 1] - offsets[g] + BM - 1) / BM : 0;
+      sum += loc[i];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int dd = 1; dd < kWave; dd <<= 1) {
+      const int o = __shfl_up(incl, dd);
+      if (lane >= dd) incl += o;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int i = 0; i < kSchedPer; ++i) {
+      const int g = lane * kSchedPer + i;
+      if (g < NG) s_mt[g] = run;
+      run += loc[i];
+    }
+    if (lane == kWave - 1) s_mt[NG] = incl;
   }
-  if (g < NG) mt_start[g + 1] = v[g];
-  if (g == 0) mt_start[0] = 0;
+  __syncthreads();
 }
 
 // Tile decode: group by binary search over mt_start * nt.
@@ -77,12 +93,13 @@ __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a));
 template <bool kSwiglu>
 __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
                                                   const float* __restrict__ B, float* __restrict__ C,
-                                                  const int32_t* __restrict__ offsets,
-                                                  const int32_t* __restrict__ mt_start, int NG,
+                                                  const int32_t* __restrict__ offsets, int NG,
                                                   int Kd, int Nrows, int Nout, int half) {
   constexpr int BM = 64, BN = 64, BK = 16;
   __shared__ __attribute__((aligned(16))) float As[BK][BM];
   __shared__ __attribute__((aligned(16))) float Bs[BK][BN];
+  __shared__ int mt_start[kMaxGroups + 1];
+  build_schedule(offsets, NG, BM, mt_start);
   const int nt = kSwiglu ? half / 32 : Nout / BN;
   const int ntiles = mt_start[NG] * nt;
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
@@ -268,10 +285,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ B,
                                                       uint16_t* __restrict__ C,
                                                       const int32_t* __restrict__ offsets,
-                                                      const int32_t* __restrict__ mt_start, int NG,
-                                                      int Kd, int Nrows, int Nout, int half) {
+                                                      int NG, int Kd, int Nrows, int Nout,
+                                                      int half) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2 * BM * LDA];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2 * BN * LDA];
+  __shared__ int mt_start[kMaxGroups + 1];
+  build_schedule(offsets, NG, BM, mt_start);
   const int nt = kSwiglu ? half / 64 : Nout / BN;
   const int ntiles = mt_start[NG] * nt;
   const int P = gridDim.x;
@@ -299,60 +318,53 @@ static int persistent_grid(int cus, int per_cu) {
 }
 
 size_t ffn_ws_bytes(const Dims& d) {
-  const size_t sched = align256(sizeof(int32_t) * (kMaxGroups + 1));
-  size_t h;
   if (d.expert == MOE_FP8_E4M3)
-    h = align256((size_t)d.R() * d.I) + align256((size_t)d.R() * (d.I / 128) * sizeof(float));
-  else
-    h = align256((size_t)d.R() * d.I * (d.expert == MOE_F32 ? 4 : 2));
-  return sched + h;
+    return align256((size_t)d.R() * d.I) + align256((size_t)d.R() * (d.I / 128) * sizeof(float));
+  return align256((size_t)d.R() * d.I * (d.expert == MOE_F32 ? 4 : 2));
 }
 
-hipError_t launch_fp8_ffn(const Dims& d, const void* xs, const float* xs_scale,
-                          const int32_t* offsets, const int32_t* mt_start, const void* w13,
-                          const float* w13_scale, const void* w2, const float* w2_scale,
-                          void* ys, void* h, float* h_scale, hipStream_t st);
+float* ffn_ws_h_scale(const Dims& d, void* ws) {
+  return reinterpret_cast<float*>(static_cast<char*>(ws) + align256((size_t)d.R() * d.I));
+}
 
-hipError_t launch_expert_ffn(const Dims& d, const void* xs, const float* xs_scale,
-                             const int32_t* offsets, const void* w13, const float* w13_scale,
-                             const void* w2, const float* w2_scale, void* ys, void* ws,
-                             hipStream_t st) {
+hipError_t launch_ffn_up(const Dims& d, const void* xs, const float* xs_scale,
+                         const int32_t* offsets, const void* w13, const float* w13_scale, void* h,
+                         float* h_scale, hipStream_t st) {
   const int NG = d.E + d.S;
-  char* base = static_cast<char*>(ws);
-  int32_t* mt_start = reinterpret_cast<int32_t*>(base);
-  void* h = base + align256(sizeof(int32_t) * (kMaxGroups + 1));
-  const int bm = d.expert == MOE_F32 ? 64 : 128;
-  hipLaunchKernelGGL(k_ffn_schedule, dim3(1), dim3(1024), 0, st, offsets, mt_start, NG, bm);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int cus = device_cu_count();
   if (d.expert == MOE_F32) {
-    const int P = persistent_grid(cus, 4);
-    hipLaunchKernelGGL(k_gemm_f32<true>, dim3(P), dim3(256), 0, st, static_cast<const float*>(xs),
-                       static_cast<const float*>(w13), static_cast<float*>(h), offsets, mt_start,
-                       NG, d.H, 2 * d.I, d.I, d.I);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_gemm_f32<false>, dim3(P), dim3(256), 0, st, static_cast<const float*>(h),
-                       static_cast<const float*>(w2), static_cast<float*>(ys), offsets, mt_start,
-                       NG, d.I, d.H, d.H, 0);
+    hipLaunchKernelGGL(k_gemm_f32<true>, dim3(persistent_grid(cus, 4)), dim3(256), 0, st,
+                       static_cast<const float*>(xs), static_cast<const float*>(w13),
+                       static_cast<float*>(h), offsets, NG, d.H, 2 * d.I, d.I, d.I);
     return hipGetLastError();
   }
   if (d.expert == MOE_BF16) {
-    const int P = persistent_grid(cus, 2);
-    hipLaunchKernelGGL(k_gemm_bf16<true>, dim3(P), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_gemm_bf16<true>, dim3(persistent_grid(cus, 2)), dim3(256), 0, st,
                        static_cast<const uint16_t*>(xs), static_cast<const uint16_t*>(w13),
-                       static_cast<uint16_t*>(h), offsets, mt_start, NG, d.H, 2 * d.I, d.I, d.I);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_gemm_bf16<false>, dim3(P), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w2),
-                       static_cast<uint16_t*>(ys), offsets, mt_start, NG, d.I, d.H, d.H, 0);
+                       static_cast<uint16_t*>(h), offsets, NG, d.H, 2 * d.I, d.I, d.I);
     return hipGetLastError();
   }
-  float* h_scale = reinterpret_cast<float*>(static_cast<char*>(h) + align256((size_t)d.R() * d.I));
-  return launch_fp8_ffn(d, xs, xs_scale, offsets, mt_start, w13, w13_scale, w2, w2_scale, ys, h,
-                        h_scale, st);
+  return launch_fp8_up(d, xs, xs_scale, offsets, w13, w13_scale, h, h_scale, st);
+}
+
+hipError_t launch_ffn_down(const Dims& d, const void* h, const float* h_scale,
+                           const int32_t* offsets, const void* w2, const float* w2_scale, void* ys,
+                           hipStream_t st) {
+  const int NG = d.E + d.S;
+  const int cus = device_cu_count();
+  if (d.expert == MOE_F32) {
+    hipLaunchKernelGGL(k_gemm_f32<false>, dim3(persistent_grid(cus, 4)), dim3(256), 0, st,
+                       static_cast<const float*>(h), static_cast<const float*>(w2),
+                       static_cast<float*>(ys), offsets, NG, d.I, d.H, d.H, 0);
+    return hipGetLastError();
+  }
+  if (d.expert == MOE_BF16) {
+    hipLaunchKernelGGL(k_gemm_bf16<false>, dim3(persistent_grid(cus, 2)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w2),
+                       static_cast<uint16_t*>(ys), offsets, NG, d.I, d.H, d.H, 0);
+    return hipGetLastError();
+  }
+  return launch_fp8_down(d, h, h_scale, offsets, w2, w2_scale, ys, st);
 }
 
 }  // namespace moe

@@ -78,10 +78,16 @@ class MoELayer:
         else:
             self.x_sorted = torch.empty((R, H), dtype=act, device=dev)
             self.x_scale = None
+        if shape.expert == "e4m3":
+            self.h = torch.empty((R, shape.I), dtype=torch.uint8, device=dev)
+            self.h_scale = torch.empty((R, shape.I // 128), dtype=torch.float32, device=dev)
+        else:
+            self.h = torch.empty((R, shape.I), dtype=act, device=dev)
+            self.h_scale = None
         self.y_sorted = torch.empty((R, H), dtype=act, device=dev)
         self.y = torch.empty((T, H), dtype=act, device=dev)
         self.ws = {}
-        for call in (L.MOE_CALL_ROUTE, L.MOE_CALL_PERMUTE, L.MOE_CALL_EXPERT_FFN):
+        for call in (L.MOE_CALL_ROUTE, L.MOE_CALL_PERMUTE):
             n = L.moe_workspace_bytes(self.p, call)
             if n == 0 and call != L.MOE_CALL_ROUTE:
                 raise L.MoeError(L.MOE_ERR_INVALID_ARG, "moe_workspace_bytes", L.last_error())
@@ -100,10 +106,17 @@ class MoELayer:
         L.moe_permute(self.p, x, self.topk_idx, self.offsets, self.sorted_token, self.inv_perm,
                       self.x_sorted, self.x_scale, ws, n, stream)
 
+    def expert_ffn_up(self, stream=None):
+        L.moe_expert_ffn_up(self.p, self.x_sorted, self.x_scale, self.offsets, self.w13,
+                            self.w13_scale, self.h, self.h_scale, stream)
+
+    def expert_ffn_down(self, stream=None):
+        L.moe_expert_ffn_down(self.p, self.h, self.h_scale, self.offsets, self.w2, self.w2_scale,
+                              self.y_sorted, stream)
+
     def expert_ffn(self, stream=None):
-        ws, n = self._ws(L.MOE_CALL_EXPERT_FFN)
-        L.moe_expert_ffn(self.p, self.x_sorted, self.x_scale, self.offsets, self.w13,
-                         self.w13_scale, self.w2, self.w2_scale, self.y_sorted, ws, n, stream)
+        self.expert_ffn_up(stream)
+        self.expert_ffn_down(stream)
 
     def combine(self, stream=None):
         L.moe_combine(self.p, self.y_sorted, self.inv_perm, self.topk_gate, self.y, stream)

@@ -20,58 +20,62 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Logits: a 64-token x 64-expert tile per 256-thread workgroup, each thread a
-// 4x4 register tile.  Hidden chunks of 32 go through LDS transposed ([h][token]
-// and [h][expert]) so one 16-byte LDS read gives a thread its 4 tokens (or 4
-// experts) at one h; every accumulator sees h in increasing order.
+// Logits: a 32-token x 64-expert tile per 128-thread workgroup (two workgroups per CU
+// at T=4096), each thread a 4x4 register tile.  Hidden chunks of 32 go through LDS
+// transposed ([h][token] and [h][expert]) so one 16-byte LDS read gives a thread its
+// 4 tokens (or 4 experts) at one h; the reads for h+1 are issued before the 16 fused
+// multiply-adds of h so LDS latency hides behind them.  Every accumulator sees h in
+// increasing order.
 // ---------------------------------------------------------------------------
-constexpr int LT = 64, LE = 64, LH = 32;
+constexpr int LT = 32, LE = 64, LH = 32, LTHREADS = 128;
 
 template <typename XT>
-__global__ __launch_bounds__(256) void k_router_logits(const XT* __restrict__ x,
-                                                       const float* __restrict__ w, float* __restrict__ z,
-                                                       int32_t* __restrict__ counts, int T, int H, int E) {
+__global__ __launch_bounds__(LTHREADS) void k_router_logits(const XT* __restrict__ x,
+                                                            const float* __restrict__ w,
+                                                            float* __restrict__ z,
+                                                            int32_t* __restrict__ counts, int T,
+                                                            int H, int E) {
   __shared__ __attribute__((aligned(16))) float xs[2][LH][LT];
   __shared__ __attribute__((aligned(16))) float wsm[2][LH][LE];
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * LT, e0 = blockIdx.y * LE;
   if (blockIdx.x == 0 && blockIdx.y == 0)
-    for (int e = tid; e < E; e += 256) counts[e] = 0;  // zeroed before the select kernel runs
+    for (int e = tid; e < E; e += LTHREADS) counts[e] = 0;  // zeroed before the select kernel
 
-  // loader mapping: 4 threads per row, 8 consecutive h each
-  const int lrow = tid >> 2, lh = (tid & 3) * 8;
-  const int xt = min(t0 + lrow, T - 1);
-  const int we = min(e0 + lrow, E - 1);
-  const XT* xp = x + (int64_t)xt * H + lh;
-  const float* wp = w + (int64_t)we * H + lh;
+  // loaders: x 32 rows x 32 h (4 threads per row, 8 h each); w 64 rows x 32 h
+  // (2 threads per row, 16 h each)
+  const int xrow = tid >> 2, xh = (tid & 3) * 8;
+  const int wrow = tid >> 1, wh = (tid & 1) * 16;
+  const XT* xp = x + (int64_t)min(t0 + xrow, T - 1) * H + xh;
+  const float* wp = w + (int64_t)min(e0 + wrow, E - 1) * H + wh;
 
-  float xr[8], wr[8];
+  float xr[8], wr[16];
   auto gload = [&](int h0) {
     if constexpr (sizeof(XT) == 2) {
-      uint4 v = *reinterpret_cast<const uint4*>(xp + h0);
-      uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      const uint4 v = *reinterpret_cast<const uint4*>(xp + h0);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         xr[2 * i] = __uint_as_float(u[i] << 16);
         xr[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
       }
     } else {
-      float4 a = *reinterpret_cast<const float4*>(xp + h0);
-      float4 b = *reinterpret_cast<const float4*>(xp + h0 + 4);
+      const float4 a = *reinterpret_cast<const float4*>(xp + h0);
+      const float4 b = *reinterpret_cast<const float4*>(xp + h0 + 4);
       xr[0] = a.x; xr[1] = a.y; xr[2] = a.z; xr[3] = a.w;
       xr[4] = b.x; xr[5] = b.y; xr[6] = b.z; xr[7] = b.w;
     }
-    float4 a = *reinterpret_cast<const float4*>(wp + h0);
-    float4 b = *reinterpret_cast<const float4*>(wp + h0 + 4);
-    wr[0] = a.x; wr[1] = a.y; wr[2] = a.z; wr[3] = a.w;
-    wr[4] = b.x; wr[5] = b.y; wr[6] = b.z; wr[7] = b.w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 a = *reinterpret_cast<const float4*>(wp + h0 + 4 * q);
+      wr[4 * q] = a.x; wr[4 * q + 1] = a.y; wr[4 * q + 2] = a.z; wr[4 * q + 3] = a.w;
+    }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xs[buf][lh + i][lrow] = xr[i];
-      wsm[buf][lh + i][lrow] = wr[i];
-    }
+    for (int i = 0; i < 8; ++i) xs[buf][xh + i][xrow] = xr[i];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wsm[buf][wh + i][wrow] = wr[i];
   };
 
   const int ty = tid >> 4, tx = tid & 15;  // tokens ty*4.., experts tx*4..
@@ -88,12 +92,16 @@ __global__ __launch_bounds__(256) void k_router_logits(const XT* __restrict__ x,
   for (int c = 0; c < nchunk; ++c) {
     const int buf = c & 1;
     if (c + 1 < nchunk) gload((c + 1) * LH);
+    float4 xv = *reinterpret_cast<const float4*>(&xs[buf][0][ty * 4]);
+    float4 wv = *reinterpret_cast<const float4*>(&wsm[buf][0][tx * 4]);
 #pragma unroll 8
     for (int hh = 0; hh < LH; ++hh) {
-      const float4 xv = *reinterpret_cast<const float4*>(&xs[buf][hh][ty * 4]);
-      const float4 wv = *reinterpret_cast<const float4*>(&wsm[buf][hh][tx * 4]);
       const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
       const float wa[4] = {wv.x, wv.y, wv.z, wv.w};
+      if (hh + 1 < LH) {
+        xv = *reinterpret_cast<const float4*>(&xs[buf][hh + 1][ty * 4]);
+        wv = *reinterpret_cast<const float4*>(&wsm[buf][hh + 1][tx * 4]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -283,10 +291,10 @@ hipError_t launch_route(const Dims& d, const void* x, const float* w_router, con
   const int T = static_cast<int>(d.T);
   dim3 g1((T + LT - 1) / LT, (d.E + LE - 1) / LE);
   if (d.act == MOE_BF16)
-    hipLaunchKernelGGL(k_router_logits<uint16_t>, g1, dim3(256), 0, st,
+    hipLaunchKernelGGL(k_router_logits<uint16_t>, g1, dim3(LTHREADS), 0, st,
                        static_cast<const uint16_t*>(x), w_router, logits, counts, T, d.H, d.E);
   else
-    hipLaunchKernelGGL(k_router_logits<float>, g1, dim3(256), 0, st,
+    hipLaunchKernelGGL(k_router_logits<float>, g1, dim3(LTHREADS), 0, st,
                        static_cast<const float*>(x), w_router, logits, counts, T, d.H, d.E);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

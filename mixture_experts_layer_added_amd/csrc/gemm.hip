@@ -164,137 +164,53 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
 }
 
 // ---------------------------------------------------------------------------
-// bf16 path: MFMA 32x32x16 (bf16 in, fp32 accumulate), 128x128 tile, 64-deep k
-// steps double-buffered in LDS with the next step's global loads in flight during
-// the current step's MFMAs.  Four waves in a 2x2 arrangement, each 2x2 MFMA tiles.
-//   kSwiglu: the tile's 128 weight rows are 64 gate rows and the matching 64 up
-//   rows; wave (wm, wn) takes gate rows 32wn.. and up rows 64+32wn.., so each lane
-//   holds the gate and up value of the same h element and applies SwiGLU in
-//   registers.
+// bf16 path: MFMA 32x32x16 (bf16 in, fp32 accumulate).
+//
+// Every weight byte comes from HBM once, while an expert's activation tile is re-read
+// (from L2) by each of its column tiles; both streams go through each CU's
+// vector-memory pipeline, where measured L2-hit bytes cost about half as much as HBM
+// bytes.  The tile is therefore shaped for few activation bytes per weight byte:
+//   - 256 rows: one tile holds all rows of an expert (82..190 at the V3 shape), so
+//     the weights never stream twice;
+//   - 256 weight rows (GEMM1: 128 gate + the matching 128 up rows): one activation
+//     read serves 256 weight rows;
+//   - activation rows past the expert's end are not fetched: the loads use a
+//     range-checked buffer descriptor sized to the expert's rows, which returns zeros
+//     with no memory traffic while every load instruction still issues.
+// One workgroup of 8 waves per CU, 4 (rows) x 2 (columns); each wave owns 64 rows x
+// 128 columns = 2 x 4 MFMA tiles and skips the MFMAs of 32-row sub-tiles past the
+// expert's rows (wave-uniform).  Operands go through LDS (double buffer); the next
+// step's global loads are in flight while the current step's MFMAs run.
+//   kSwiglu: wave column wn owns gate rows 64wn..64wn+63 of the tile and the matching
+//   up rows, so each lane holds the gate and up value of the same h element and
+//   applies SwiGLU in registers.
 // Operand layout (32x32x16): lane l supplies row (l%32), k = 8*(l/32)..+7 of A and
 // column (l%32), the same k of B; result element i of lane l is row
 // 8*(i/4) + 4*(l/32) + i%4, column l%32.
 // ---------------------------------------------------------------------------
-constexpr int BM = 128, BN = 128, BK = 64, LDA = BK + 8;
+constexpr int BM = 256, BN = 256, BK = 64, LDA = BK + 8;
 
 template <bool kSwiglu>
-__device__ __forceinline__ void gemm_bf16_tile(const uint16_t* __restrict__ A,
-                                               const uint16_t* __restrict__ B,
-                                               uint16_t* __restrict__ C, uint16_t* As, uint16_t* Bs,
-                                               const Tile& tl, int row0, int m_g, int Kd,
-                                               int Nrows, int Nout, int half) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
-  const int nk = Kd / BK;
-  const int m0 = tl.m_idx * BM;
-
-  // loader: chunk c = tid + 256*i -> row c/8, 8 bf16 at k (c%8)*8
-  int64_t aoff[4], boff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c >> 3, kc = (c & 7) * 8;
-    aoff[i] = (int64_t)(row0 + min(m0 + r, m_g - 1)) * Kd + kc;
-    int brow;
-    if (kSwiglu) brow = r < 64 ? tl.n_idx * 64 + r : half + tl.n_idx * 64 + (r - 64);
-    else brow = tl.n_idx * BN + r;
-    boff[i] = ((int64_t)tl.g * Nrows + brow) * Kd + kc;
-  }
-  const int soff = (tid >> 3) * LDA + (tid & 7) * 8;  // + 32*LDA per i
-  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-#define GEMM_GLOAD(k0)                                                  \
-  ra0 = *reinterpret_cast<const uint4*>(A + aoff[0] + (k0));            \
-  ra1 = *reinterpret_cast<const uint4*>(A + aoff[1] + (k0));            \
-  ra2 = *reinterpret_cast<const uint4*>(A + aoff[2] + (k0));            \
-  ra3 = *reinterpret_cast<const uint4*>(A + aoff[3] + (k0));            \
-  rb0 = *reinterpret_cast<const uint4*>(B + boff[0] + (k0));            \
-  rb1 = *reinterpret_cast<const uint4*>(B + boff[1] + (k0));            \
-  rb2 = *reinterpret_cast<const uint4*>(B + boff[2] + (k0));            \
-  rb3 = *reinterpret_cast<const uint4*>(B + boff[3] + (k0));
-#define GEMM_LSTORE(buf)                                                          \
-  *reinterpret_cast<uint4*>(As + (buf) * BM * LDA + soff) = ra0;                  \
-  *reinterpret_cast<uint4*>(As + (buf) * BM * LDA + soff + 32 * LDA) = ra1;       \
-  *reinterpret_cast<uint4*>(As + (buf) * BM * LDA + soff + 64 * LDA) = ra2;       \
-  *reinterpret_cast<uint4*>(As + (buf) * BM * LDA + soff + 96 * LDA) = ra3;       \
-  *reinterpret_cast<uint4*>(Bs + (buf) * BN * LDA + soff) = rb0;                  \
-  *reinterpret_cast<uint4*>(Bs + (buf) * BN * LDA + soff + 32 * LDA) = rb1;       \
-  *reinterpret_cast<uint4*>(Bs + (buf) * BN * LDA + soff + 64 * LDA) = rb2;       \
-  *reinterpret_cast<uint4*>(Bs + (buf) * BN * LDA + soff + 96 * LDA) = rb3;
-
-  f32x16 acc00, acc01, acc10, acc11;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    acc00[i] = 0.0f; acc01[i] = 0.0f; acc10[i] = 0.0f; acc11[i] = 0.0f;
-  }
-  const int a_row = 64 * wm + (lane & 31);
-  const int b_row0 = kSwiglu ? 32 * wn + (lane & 31) : 64 * wn + (lane & 31);
-  const int b_row1 = b_row0 + (kSwiglu ? 64 : 32);
-  const int kq = (lane >> 5) * 8;
-
-  GEMM_GLOAD(0)
-  GEMM_LSTORE(0)
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) {
-      GEMM_GLOAD((kt + 1) * BK)
-    }
-    const uint16_t* as = As + buf * BM * LDA;
-    const uint16_t* bs = Bs + buf * BN * LDA;
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(as + a_row * LDA + 16 * s + kq);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(as + (a_row + 32) * LDA + 16 * s + kq);
-      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(bs + b_row0 * LDA + 16 * s + kq);
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(bs + b_row1 * LDA + 16 * s + kq);
-      acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc00, 0, 0, 0);
-      acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc01, 0, 0, 0);
-      acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc10, 0, 0, 0);
-      acc11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc11, 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-      GEMM_LSTORE(buf ^ 1)
-    }
-    __syncthreads();
-  }
-#undef GEMM_GLOAD
-#undef GEMM_LSTORE
-
-  // epilogue: rows 64wm + 32mi + 8(i/4) + 4(l/32) + i%4, column l%32 of the sub-tile
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    const f32x16& c0 = mi ? acc10 : acc00;
-    const f32x16& c1 = mi ? acc11 : acc01;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = m0 + 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      if (m >= m_g) continue;
-      uint16_t* cp = C + (int64_t)(row0 + m) * Nout;
-      if (kSwiglu) {
-        cp[tl.n_idx * 64 + 32 * wn + (lane & 31)] = f32_to_bf16_bits(silu(c0[i]) * c1[i]);
-      } else {
-        cp[tl.n_idx * BN + 64 * wn + (lane & 31)] = f32_to_bf16_bits(c0[i]);
-        cp[tl.n_idx * BN + 64 * wn + 32 + (lane & 31)] = f32_to_bf16_bits(c1[i]);
-      }
-    }
-  }
-}
-
-template <bool kSwiglu>
-__global__ __launch_bounds__(256, 2) void k_gemm_bf16(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict__ A,
                                                       const uint16_t* __restrict__ B,
                                                       uint16_t* __restrict__ C,
                                                       const int32_t* __restrict__ offsets,
                                                       int NG, int Kd, int Nrows, int Nout,
                                                       int half) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2 * BM * LDA];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2 * BN * LDA];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDA];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDA];
   __shared__ int mt_start[kMaxGroups + 1];
   build_schedule(offsets, NG, BM, mt_start);
-  const int nt = kSwiglu ? half / 64 : Nout / BN;
+  const int nt = kSwiglu ? half / 128 : (Nout + BN - 1) / BN;
   const int ntiles = mt_start[NG] * nt;
-  const int P = gridDim.x;
-  const int per_xcd = P / kXcds;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv & 3, wn = wv >> 2;
+  const int nk = Kd / BK;
+  const int lr = tid >> 3, lc = (tid & 7) * 8;  // loader rows lr + 64*i
+  const int kq = (lane >> 5) * 8;
+  const int sA = lr * LDA + lc;
+
+  const int P = gridDim.x, per_xcd = P / kXcds;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int chunk = (ntiles + kXcds - 1) / kXcds;
   const int end = min(ntiles, (xcd + 1) * chunk);
@@ -302,7 +218,131 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(const uint16_t* __restrict
     const Tile tl = decode_tile(tile, mt_start, NG, nt);
     const int row0 = offsets[tl.g];
     const int m_g = offsets[tl.g + 1] - row0;
-    gemm_bf16_tile<kSwiglu>(A, B, C, As, Bs, tl, row0, m_g, Kd, Nrows, Nout, half);
+    const int m0 = tl.m_idx * BM;
+    const int m_rows = min(BM, m_g - m0);
+    const bool w_on = 64 * wm < m_rows && (kSwiglu || tl.n_idx * BN + 128 * wn < Nout);
+    const bool w_sub1 = 64 * wm + 32 < m_rows;
+
+    const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(A + (int64_t)(row0 + m0) * Kd), (short)0, m_rows * Kd * 2, 0x00020000);
+    const int aoff = (lr * Kd + lc) * 2;
+    const int arow64 = 64 * Kd * 2;
+    int br[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = lr + 64 * i;
+      br[i] = kSwiglu ? (r < 128 ? tl.n_idx * 128 + r : half + tl.n_idx * 128 + (r - 128))
+                      : min(tl.n_idx * BN + r, Nout - 1);
+    }
+    const uint16_t* bbase = B + (int64_t)tl.g * Nrows * Kd + lc;
+    const int64_t bo0 = (int64_t)br[0] * Kd, bo1 = (int64_t)br[1] * Kd;
+    const int64_t bo2 = (int64_t)br[2] * Kd, bo3 = (int64_t)br[3] * Kd;
+
+    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+#define A_LD(i, k)                                                                          \
+  ({                                                                                        \
+    auto v_ = __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff + (i) * arow64 + (k) * BK * 2, \
+                                                    0, 0);                                  \
+    *reinterpret_cast<uint4*>(&v_);                                                         \
+  })
+#define G_LD(p) (*reinterpret_cast<const uint4*>(p))
+#define GEMM_GLOAD(k)                                                         \
+  {                                                                           \
+    ra0 = A_LD(0, k); ra1 = A_LD(1, k); ra2 = A_LD(2, k); ra3 = A_LD(3, k);   \
+    const int ko = (k) * BK;                                                  \
+    rb0 = G_LD(bbase + bo0 + ko); rb1 = G_LD(bbase + bo1 + ko);               \
+    rb2 = G_LD(bbase + bo2 + ko); rb3 = G_LD(bbase + bo3 + ko);               \
+  }
+#define GEMM_LSTORE(buf)                                                      \
+  {                                                                           \
+    uint16_t* ad = &As[buf][sA];                                              \
+    uint16_t* bd = &Bs[buf][sA];                                              \
+    *reinterpret_cast<uint4*>(ad) = ra0;                                      \
+    if (m_rows > 64) *reinterpret_cast<uint4*>(ad + 64 * LDA) = ra1;          \
+    if (m_rows > 128) *reinterpret_cast<uint4*>(ad + 128 * LDA) = ra2;        \
+    if (m_rows > 192) *reinterpret_cast<uint4*>(ad + 192 * LDA) = ra3;        \
+    *reinterpret_cast<uint4*>(bd) = rb0;                                      \
+    *reinterpret_cast<uint4*>(bd + 64 * LDA) = rb1;                           \
+    *reinterpret_cast<uint4*>(bd + 128 * LDA) = rb2;                          \
+    *reinterpret_cast<uint4*>(bd + 192 * LDA) = rb3;                          \
+  }
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mi][n][i] = 0.0f;
+    // B sub-tile rows of this wave: swiglu gate 64wn + 32t, up 128 + 64wn + 32t (t = 0,1);
+    // plain 128wn + 32n
+    int brow[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+      brow[n] = (kSwiglu ? ((n & 1) * 128 + 64 * wn + 32 * (n >> 1)) : (128 * wn + 32 * n)) +
+                (lane & 31);
+    const int a_row = 64 * wm + (lane & 31);
+
+    GEMM_GLOAD(0)
+    GEMM_LSTORE(0)
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) {
+        GEMM_GLOAD(kt + 1)
+      }
+      if (w_on) {
+        const uint16_t* as = As[buf];
+        const uint16_t* bs = Bs[buf];
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
+          bf16x8 b[4];
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            b[n] = *reinterpret_cast<const bf16x8*>(bs + brow[n] * LDA + 16 * s + kq);
+          const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(as + a_row * LDA + 16 * s + kq);
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            acc[0][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[n], acc[0][n], 0, 0, 0);
+          if (w_sub1) {
+            const bf16x8 a1 =
+                *reinterpret_cast<const bf16x8*>(as + (a_row + 32) * LDA + 16 * s + kq);
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+              acc[1][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[n], acc[1][n], 0, 0, 0);
+          }
+        }
+      }
+      if (kt + 1 < nk) {
+        GEMM_LSTORE(buf ^ 1)
+      }
+      __syncthreads();
+    }
+#undef A_LD
+#undef G_LD
+#undef GEMM_GLOAD
+#undef GEMM_LSTORE
+
+    if (w_on) {
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          if (m >= m_rows) continue;
+          uint16_t* cp = C + (int64_t)(row0 + m0 + m) * Nout;
+          if (kSwiglu) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+              cp[tl.n_idx * 128 + 64 * wn + 32 * t + (lane & 31)] =
+                  f32_to_bf16_bits(silu(acc[mi][2 * t][i]) * acc[mi][2 * t + 1][i]);
+          } else {
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+              cp[tl.n_idx * BN + 128 * wn + 32 * n + (lane & 31)] = f32_to_bf16_bits(acc[mi][n][i]);
+          }
+        }
+    }
   }
 }
 
@@ -339,7 +379,7 @@ hipError_t launch_ffn_up(const Dims& d, const void* xs, const float* xs_scale,
     return hipGetLastError();
   }
   if (d.expert == MOE_BF16) {
-    hipLaunchKernelGGL(k_gemm_bf16<true>, dim3(persistent_grid(cus, 2)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_gemm_bf16<true>, dim3(persistent_grid(cus, 1)), dim3(512), 0, st,
                        static_cast<const uint16_t*>(xs), static_cast<const uint16_t*>(w13),
                        static_cast<uint16_t*>(h), offsets, NG, d.H, 2 * d.I, d.I, d.I);
     return hipGetLastError();
@@ -359,7 +399,7 @@ hipError_t launch_ffn_down(const Dims& d, const void* h, const float* h_scale,
     return hipGetLastError();
   }
   if (d.expert == MOE_BF16) {
-    hipLaunchKernelGGL(k_gemm_bf16<false>, dim3(persistent_grid(cus, 2)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_gemm_bf16<false>, dim3(persistent_grid(cus, 1)), dim3(512), 0, st,
                        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w2),
                        static_cast<uint16_t*>(ys), offsets, NG, d.I, d.H, d.H, 0);
     return hipGetLastError();

@@ -1,0 +1,180 @@
+"""GPU parity at the full DeepSeek-V3 layer shape (hidden 7168, 256 routed experts + 1
+shared, top-8 of 8 groups with at most 4 per token, SwiGLU width 2048), in the launch
+configuration the benchmark times.
+
+The oracle recomputes everything it can at full size: routing of every token (logits,
+indices, gates, counts bit for bit) and the permutation; the expert FFN and the combine
+are checked on sampled tokens, which the oracle computes one by one from the inputs and
+its own routing.  The skewed balancing loop compares the bias bit for bit at each of 50
+steps.
+"""
+import concurrent.futures as cf
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_cases import TOL, as_f64, log, shape_of
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mixture_experts_layer_added_amd import _lib
+    _lib.lib()
+    yield
+    torch.cuda.empty_cache()
+
+
+def np_(t):
+    return workloads.to_numpy(t)
+
+
+def build(w, fp8=False):
+    from mixture_experts_layer_added_amd.layer import MoELayer, quantize_weights_fp8
+    dev = torch.device("cuda")
+    wr, b = workloads.make_router(w, dev)
+    w13, w2 = workloads.make_experts(w, dev)
+    s13 = s2 = None
+    if fp8:
+        q13, s13 = quantize_weights_fp8(w13)
+        q2, s2 = quantize_weights_fp8(w2)
+        return MoELayer(shape_of(w), wr, b, q13, q2, s13, s2), (w13, w2)
+    return MoELayer(shape_of(w), wr, b, w13, w2), (w13, w2)
+
+
+def check_routing(w, layer, x):
+    """Full-size routing and permutation against the oracle (bit for bit).
+    Returns the oracle's routing."""
+    xn = np_(x)
+    idx, gate, counts, z = oracle.route(xn, np_(layer.w_router), np_(layer.bias), w.G, w.M, w.K,
+                                        w.J, want_logits=True)
+    assert np.array_equal(np_(layer.logits).view(np.uint32), z.view(np.uint32))
+    assert np.array_equal(np_(layer.topk_idx), idx)
+    assert np.array_equal(np_(layer.topk_gate).view(np.uint32), gate.view(np.uint32))
+    assert np.array_equal(np_(layer.counts), counts)
+    fp8 = w.expert == "e4m3"
+    off, st, inv, xs, xsc = oracle.permute(xn, idx, counts, w.E, w.S,
+                                           out_dtype=oracle.E4M3 if fp8 else None)
+    assert np.array_equal(np_(layer.offsets), off)
+    assert np.array_equal(np_(layer.sorted_token), st)
+    assert np.array_equal(np_(layer.inv_perm), inv)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([rng.integers(0, w.R, 3000), [0, w.R - 1, w.T * w.K]]))
+    got = np_(layer.x_sorted[torch.from_numpy(rows).cuda()])
+    assert np.array_equal(got.view(np.uint8), xs[rows].view(np.uint8))
+    if fp8:
+        gsc = np_(layer.x_scale[torch.from_numpy(rows).cuda()])
+        assert np.array_equal(gsc.view(np.uint32), xsc[rows].view(np.uint32))
+    log(f"    routing/permutation bit-exact for all {w.T} tokens; "
+        f"loads min/max {counts.min()}/{counts.max()} (mean {w.T * w.K / w.E:.1f})")
+    return idx, gate, counts, inv, xs, xsc
+
+
+def sampled_tokens(w, n, seed=0):
+    rng = np.random.default_rng(seed)
+    t = rng.choice(w.T, size=min(n, w.T), replace=False)
+    return np.unique(np.concatenate([t, [0, w.T - 1]]))[: n + 2]
+
+
+def check_sampled_outputs(w, layer, idx, gate, inv, xs, xsc, wts, tokens):
+    """Oracle expert outputs and combined outputs of the sampled tokens vs the GPU's."""
+    fp8 = w.expert == "e4m3"
+    groups = sorted(set(int(e) for t in tokens for e in idx[t]) | {w.E})
+    out_dt = oracle.BF16 if w.act == "bf16" else oracle.F32
+    # oracle rows: (t, group) -> row of x_sorted
+    work = {}
+    for t in tokens:
+        for k in range(w.K):
+            work.setdefault(int(idx[t, k]), []).append(int(inv[t, k]))
+        work.setdefault(w.E, []).append(w.T * w.K + int(t))
+    if fp8:
+        w13b, w2b = wts
+
+    def one(g):
+        rows = np.array(work[g])
+        if fp8:
+            a, sa = oracle.quantize_weight_fp8(np_(w13b[g]))
+            b, sb = oracle.quantize_weight_fp8(np_(w2b[g]))
+            assert np.array_equal(np_(layer.w13[g]), a)
+            assert np.array_equal(np_(layer.w13_scale[g]).view(np.uint32), sa.view(np.uint32))
+            assert np.array_equal(np_(layer.w2[g]), b)
+            assert np.array_equal(np_(layer.w2_scale[g]).view(np.uint32), sb.view(np.uint32))
+            y = oracle.expert_ffn(xs[rows], a, b, out_dt, xsc[rows], sa, sb, nthreads=1)
+        else:
+            y = oracle.expert_ffn(xs[rows], np_(layer.w13[g]), np_(layer.w2[g]), out_dt, nthreads=1)
+        return g, rows, y
+
+    ref_rows = {}
+    with cf.ThreadPoolExecutor(oracle.default_threads()) as ex:
+        for g, rows, y in ex.map(one, groups):
+            for r, yr in zip(rows, y):
+                ref_rows[int(r)] = yr
+    allrows = np.array(sorted(ref_rows))
+    ref = np.stack([ref_rows[r] for r in allrows])
+    got = np_(layer.y_sorted[torch.from_numpy(allrows).cuda()])
+    e1 = float(np.abs(as_f64(got, w.act) - as_f64(ref, w.act)).max() / np.abs(as_f64(ref, w.act)).max())
+    # combine of the sampled tokens from the oracle's rows, in the oracle's order
+    n = len(tokens)
+    mini = np.zeros((n * w.K + n, w.H), ref.dtype)
+    mini_inv = np.zeros((n, w.K), np.int32)
+    for i, t in enumerate(tokens):
+        for k in range(w.K):
+            mini[i * w.K + k] = ref_rows[int(inv[t, k])]
+            mini_inv[i, k] = i * w.K + k
+        mini[n * w.K + i] = ref_rows[w.T * w.K + int(t)]
+    yref = oracle.combine(mini, mini_inv, np.ascontiguousarray(gate[tokens]), n, w.S)
+    ygot = np_(layer.y[torch.from_numpy(tokens).cuda()])
+    dy = np.abs(as_f64(ygot, w.act) - as_f64(yref, w.act)).max()
+    e2 = float(dy / (2 * np.abs(as_f64(ref, w.act)).max()))
+    log(f"    sampled {n} tokens ({len(allrows)} expert rows): y_sorted rel err {e1:.3e}, "
+        f"y err / (2 max|Y|) {e2:.3e} (bound {TOL[w.expert]})")
+    assert e1 <= TOL[w.expert] and e2 <= TOL[w.expert]
+
+
+@pytest.mark.parametrize("name,n_tok", [("v3-bf16", 10), ("v3-decode", 8), ("v3-fp8", 6)])
+def test_full_shape_forward(name, n_tok):
+    w = workloads.get(name)
+    log(f"[full] {name}: T={w.T} H={w.H} E={w.E}+{w.S} K={w.K} I={w.I} expert={w.expert}")
+    layer, wts = build(w, fp8=w.expert == "e4m3")
+    x = workloads.make_x(w, device="cuda")
+    layer.forward(x)
+    torch.cuda.synchronize()
+    idx, gate, counts, inv, xs, xsc = check_routing(w, layer, x)
+    check_sampled_outputs(w, layer, idx, gate, inv, xs, xsc, wts, sampled_tokens(w, n_tok))
+    del layer, wts, x
+    torch.cuda.empty_cache()
+
+
+def test_skew_loop_bias_trajectory():
+    """50 forward + bias-update steps on fresh seeded x with Zipf-skewed router logits:
+    the GPU and oracle biases agree bit for bit after every step."""
+    w = workloads.get("v3-skew-loop")
+    log(f"[skew loop] T={w.T}, {w.steps} steps, gamma={w.gamma}")
+    layer, _ = build(w)
+    wr = np_(layer.w_router)
+    b_ref = np_(layer.bias).copy()
+    ratios = []
+    for step in range(w.steps):
+        x = workloads.make_x(w, step=step, device="cuda")
+        layer.step(x, w.gamma)
+        _, _, counts, _ = oracle.route(np_(x), wr, b_ref, w.G, w.M, w.K, w.J)
+        b_ref = oracle.bias_update(counts, w.T, w.K, w.gamma, b_ref)
+        torch.cuda.synchronize()
+        assert np.array_equal(np_(layer.counts), counts), step
+        assert np.array_equal(np_(layer.bias).view(np.uint32), b_ref.view(np.uint32)), step
+        ratios.append(counts.max() / (w.T * w.K / w.E))
+        if step % 10 == 0 or step == w.steps - 1:
+            log(f"    step {step:2d}: max/mean load {ratios[-1]:.3f}, top-16 share "
+                f"{workloads.zipf_top16_share(counts):.3f}, bias range "
+                f"[{b_ref.min():+.2f}, {b_ref.max():+.2f}]")
+    log("    max/mean per step: " + " ".join(f"{r:.2f}" for r in ratios))
+    # the balancing pushes the load toward uniform (the pages describe this qualitatively)
+    assert ratios[-1] < ratios[0]
+    del layer
+    torch.cuda.empty_cache()

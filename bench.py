@@ -16,8 +16,10 @@ oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -34,6 +36,34 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def kernel_source_sha(expert):
+    """sha256 over the sources that define the gate/up GEMM of this expert dtype."""
+    csrc = os.path.join(ROOT, "mixture_experts_layer_added_amd", "csrc")
+    files = ["gemm_fp8.hip" if expert == "e4m3" else "gemm.hip", "common.h"]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, expert):
+    """HBM bytes per gate/up launch from the committed FETCH_SIZE / WRITE_SIZE counter
+    summary of this workload, or None when there is none or the kernel source has changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"ffn_up_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    with open(path) as fh:
+        m = re.search(r"^traffic: (\{.*\})$", fh.read(), re.M)
+    if not m:
+        return None, "counter summary unreadable"
+    rec = json.loads(m.group(1))
+    if rec.get("source_sha256") != kernel_source_sha(expert):
+        return None, "kernel changed since the counters were taken"
+    return int(rec["fetch_bytes"] + rec["write_bytes"]), path[len(ROOT) + 1:]
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -42,7 +72,7 @@ def parse():
     ap.add_argument("--workload", default="v3-bf16")
     ap.add_argument("--tokens", type=int, default=0, help="override T of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-ffn-rows", type=int, default=512,
+    ap.add_argument("--cpu-ffn-rows", type=int, default=2048,
                     help="expert-FFN rows the oracle computes for its sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this size (for counter calibration)")
@@ -188,6 +218,10 @@ def main():
                 "unit": "GB/s", "frac": round(up_gbs / HBM_PEAK_GBS, 4),
                 "bytes_per_launch": up_bytes, "ms_per_launch": round(avg_ms["ffn_up"], 4),
                 "traffic": None}
+    traffic, src = measured_traffic(w.name, w.expert)
+    roofline["traffic"] = traffic
+    roofline["traffic_source"] = src
+    roofline["kernel_source_sha256"] = kernel_source_sha(w.expert)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20)
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -244,31 +278,38 @@ def cpu_baseline(w, layer, x, w_router, bias, w13, w2, ffn_rows):
     off, st, inv, xs, xsc = oracle.permute(xn, idx, counts, w.E, w.S,
                                            out_dtype=oracle.E4M3 if fp8 else None)
     t_perm = time.perf_counter() - t
-    # FFN sample: rows of expert 0 and of the shared expert
+    # FFN sample: ffn_rows/2 routed rows (whole experts, in index order) and ffn_rows/2
+    # rows of the shared expert
     half = ffn_rows // 2
-    g0 = int(np.argmax(counts > 0))
-    rows0 = np.arange(off[g0], min(off[g0 + 1], off[g0] + half))
-    rows_s = np.arange(off[w.E], off[w.E] + half)
-    if fp8:
-        q13, s13, q2, s2 = w13
-        wq = {g: (workloads.to_numpy(q13[g]), workloads.to_numpy(s13[g]),
-                  workloads.to_numpy(q2[g]), workloads.to_numpy(s2[g])) for g in (g0, w.E)}
-    else:
-        wq = {g: (workloads.to_numpy(w13[g]), workloads.to_numpy(w2[g])) for g in (g0, w.E)}
+    sample = []
+    taken = 0
+    for g in range(w.E):
+        if taken >= half:
+            break
+        n = min(int(off[g + 1] - off[g]), half - taken)
+        if n > 0:
+            sample.append((g, np.arange(off[g], off[g] + n)))
+            taken += n
+    sample.append((w.E, np.arange(off[w.E], off[w.E] + half)))
     out_dt = oracle.BF16 if w.act == "bf16" else oracle.F32
-    t = time.perf_counter()
+    t_ffn_sample = 0.0
     n_rows = 0
-    for g, rows in ((g0, rows0), (w.E, rows_s)):
+    for g, rows in sample:
         if fp8:
-            a, sa, b, sb = wq[g]
+            q13, s13, q2, s2 = w13
+            a, sa, b, sb = (workloads.to_numpy(q13[g]), workloads.to_numpy(s13[g]),
+                            workloads.to_numpy(q2[g]), workloads.to_numpy(s2[g]))
+            t = time.perf_counter()
             oracle.expert_ffn(xs[rows], a, b, out_dt, xsc[rows], sa, sb, nthreads=threads)
         else:
-            a, b = wq[g]
+            a, b = workloads.to_numpy(w13[g]), workloads.to_numpy(w2[g])
+            t = time.perf_counter()
             oracle.expert_ffn(xs[rows], a, b, out_dt, nthreads=threads)
+        t_ffn_sample += time.perf_counter() - t
         n_rows += len(rows)
-    t_ffn_sample = time.perf_counter() - t
+    experts = f"experts {sample[0][0]}..{sample[-2][0]} and the shared expert"
     t_ffn = t_ffn_sample * (w.R / n_rows)
-    ys = workloads.to_numpy(workloads.make_y_sorted(w, seed=9, device="cuda"))
+    ys = workloads.to_numpy(workloads.make_y_sorted(w, seed=9, device=x.device))
     t = time.perf_counter()
     oracle.combine(ys, inv, gate, w.T, w.S, nthreads=threads)
     t_comb = time.perf_counter() - t
@@ -282,7 +323,7 @@ def cpu_baseline(w, layer, x, w_router, bias, w13, w2, ffn_rows):
     return {"value": round(w.T / total, 3), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": (f"route+permute+combine+bias of all {w.T} tokens; expert FFN on "
-                       f"{n_rows} rows (expert {g0} and the shared expert) scaled to the "
+                       f"{n_rows} rows ({experts}) scaled to the "
                        f"{w.R} rows of the batch; {measured:.1f}s measured"),
             "seconds_per_step_extrapolated": round(total, 2)}
 

@@ -33,7 +33,8 @@
  *     library keeps no mutable global state apart from the per-thread error string.
  *
  * Problem limits (checked): 1 <= T, T*(K+1) < 2^31; H % 128 == 0, 128 <= H <= 65536;
- * I % 128 == 0, 128 <= I <= 32768; 1 <= E <= 512, E % G == 0, 1 <= G <= 64,
+ * I % 128 == 0, 128 <= I <= 32768, H*I <= 2^28 (one expert's weights addressed with
+ * 32-bit byte offsets); 1 <= E <= 512, E % G == 0, 1 <= G <= 64,
  * 1 <= M <= G, 1 <= J <= min(E/G, 8), 1 <= K <= min(M*E/G, 16); S in {0, 1}.
  * Dtypes: act_dtype F32 with expert_dtype F32, or act_dtype BF16 with expert_dtype
  * BF16 or FP8_E4M3.  Inputs must be finite.

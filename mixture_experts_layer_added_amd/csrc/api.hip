@@ -61,6 +61,9 @@ moe_status validate(const moe_problem* p, Dims* d) {
     return fail(MOE_ERR_INVALID_ARG, "H=%d must be a multiple of 128 in [128,65536]", p->H);
   if (p->I < 128 || p->I > 32768 || p->I % 128)
     return fail(MOE_ERR_INVALID_ARG, "I=%d must be a multiple of 128 in [128,32768]", p->I);
+  if ((int64_t)p->H * p->I > ((int64_t)1 << 28))
+    return fail(MOE_ERR_INVALID_ARG, "H*I=%lld must be <= 2^28 (32-bit buffer offsets)",
+                (long long)p->H * p->I);
   if (p->E < 1 || p->E > 512) return fail(MOE_ERR_INVALID_ARG, "E=%d must be in [1,512]", p->E);
   if (p->G < 1 || p->G > 64 || p->E % p->G)
     return fail(MOE_ERR_INVALID_ARG, "G=%d must divide E=%d and be in [1,64]", p->G, p->E);

@@ -167,20 +167,22 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
 // bf16 path: MFMA 32x32x16 (bf16 in, fp32 accumulate).
 //
 // Every weight byte comes from HBM once, while an expert's activation tile is re-read
-// (from L2) by each of its column tiles; both streams go through each CU's
-// vector-memory pipeline, where measured L2-hit bytes cost about half as much as HBM
-// bytes.  The tile is therefore shaped for few activation bytes per weight byte:
-//   - 256 rows: one tile holds all rows of an expert (82..190 at the V3 shape), so
+// (from L2) by each of its column tiles.  The tile is shaped for that:
+//   - 256 rows: one tile holds all rows of an expert (73..193 at the V3 shape), so
 //     the weights never stream twice;
 //   - 256 weight rows (GEMM1: 128 gate + the matching 128 up rows): one activation
 //     read serves 256 weight rows;
-//   - activation rows past the expert's end are not fetched: the loads use a
-//     range-checked buffer descriptor sized to the expert's rows, which returns zeros
-//     with no memory traffic while every load instruction still issues.
-// One workgroup of 8 waves per CU, 4 (rows) x 2 (columns); each wave owns 64 rows x
-// 128 columns = 2 x 4 MFMA tiles and skips the MFMAs of 32-row sub-tiles past the
-// expert's rows (wave-uniform).  Operands go through LDS (double buffer); the next
-// step's global loads are in flight while the current step's MFMAs run.
+//   - 64-deep k steps: every row of a step is one full 128-byte line (narrower row
+//     segments cost far more memory-pipeline time per byte on this GPU).
+// Operands go from memory straight into LDS (buffer loads with the LDS destination
+// bit, no register staging).  The LDS ring is shaped per tile: the A stage holds
+// ceil(rows/64)*64 rows, and when a stage fits three times into 144 KiB (experts of
+// <= 128 rows) two steps are in flight while one is multiplied, else one.
+// Activation rows past the expert's end are read through a buffer descriptor sized
+// to the expert's rows, so they arrive as zeros with no memory traffic.
+// One workgroup of 8 waves per CU: wave w owns rows 64*(w/2) .. +63 and columns
+// 128*(w%2) .. +127 (2 x 4 MFMA tiles), so the waves with rows sit on all four SIMDs;
+// MFMAs of 32-row sub-tiles past the expert's rows are skipped (wave-uniform).
 //   kSwiglu: wave column wn owns gate rows 64wn..64wn+63 of the tile and the matching
 //   up rows, so each lane holds the gate and up value of the same h element and
 //   applies SwiGLU in registers.
@@ -188,7 +190,46 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
 // column (l%32), the same k of B; result element i of lane l is row
 // 8*(i/4) + 4*(l/32) + i%4, column l%32.
 // ---------------------------------------------------------------------------
-constexpr int BM = 256, BN = 256, BK = 64, LDA = BK + 8;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kRowBytes = BK * 2;               // one row of one stage: a full 128-B line
+constexpr int kBStage = BN * kRowBytes;         // 32 KiB
+constexpr int kRing = 3 * (128 * kRowBytes + kBStage);  // 144 KiB
+
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  i32x4 r;
+  r.x = (int)(uint32_t)a;
+  r.y = (int)((uint32_t)(a >> 32) & 0xffffu);
+  r.z = (int)bytes;
+  r.w = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16*lane.
+__device__ __forceinline__ void load_to_lds(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               ::"s"(lds), "v"(voff), "s"(rsrc) : "memory");
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding.
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+}
+
+// byte offset of (row, 16-byte k-chunk c) inside an operand stage: rows of 128 B,
+// chunk slots xor-swizzled by (row >> 1) & 7 so 16 consecutive rows at one chunk hit
+// 16 distinct bank groups
+__device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ (r >> 1)) & 7) * 16; }
 
 template <bool kSwiglu>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict__ A,
@@ -197,74 +238,72 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
                                                       const int32_t* __restrict__ offsets,
                                                       int NG, int Kd, int Nrows, int Nout,
                                                       int half) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDA];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDA];
+  __shared__ __attribute__((aligned(1024))) char smem[kRing];
   __shared__ int mt_start[kMaxGroups + 1];
   build_schedule(offsets, NG, BM, mt_start);
   const int nt = kSwiglu ? half / 128 : (Nout + BN - 1) / BN;
   const int ntiles = mt_start[NG] * nt;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv & 3, wn = wv >> 2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv >> 1, wn = wv & 1;
   const int nk = Kd / BK;
-  const int lr = tid >> 3, lc = (tid & 7) * 8;  // loader rows lr + 64*i
-  const int kq = (lane >> 5) * 8;
-  const int sA = lr * LDA + lc;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
+  // loader: instruction i of wave wv fills rows 64i + 8wv .. +7 of an operand stage;
+  // lane l writes row 64i + 8wv + (l>>3), slot l&7, which holds k-chunk
+  // (l&7) ^ ((row>>1)&7); (row>>1)&7 = (4*(wv&1) + (l>>4)) & 7
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ ((4 * (wv & 1) + (lane >> 4)) & 7);
+  const int kq = lane >> 5;
 
   const int P = gridDim.x, per_xcd = P / kXcds;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int chunk = (ntiles + kXcds - 1) / kXcds;
   const int end = min(ntiles, (xcd + 1) * chunk);
   for (int tile = xcd * chunk + slot; tile < end; tile += per_xcd) {
-    const Tile tl = decode_tile(tile, mt_start, NG, nt);
+    Tile tl = decode_tile(tile, mt_start, NG, nt);
+    tl.g = __builtin_amdgcn_readfirstlane(tl.g);
+    tl.n_idx = __builtin_amdgcn_readfirstlane(tl.n_idx);
+    tl.m_idx = __builtin_amdgcn_readfirstlane(tl.m_idx);
     const int row0 = offsets[tl.g];
     const int m_g = offsets[tl.g + 1] - row0;
     const int m0 = tl.m_idx * BM;
     const int m_rows = min(BM, m_g - m0);
     const bool w_on = 64 * wm < m_rows && (kSwiglu || tl.n_idx * BN + 128 * wn < Nout);
     const bool w_sub1 = 64 * wm + 32 < m_rows;
+    // ring shape of this tile: A stage holds nA*64 rows; three stages when they fit
+    const int nA = (m_rows + 63) >> 6;
+    const int sA = nA * 64 * kRowBytes;
+    const int sStage = sA + kBStage;
+    const int nst = (3 * sStage <= kRing) ? 3 : 2;
+    const int per_stage = nA + 4;  // loads per thread per stage
 
-    const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(A + (int64_t)(row0 + m0) * Kd), (short)0, m_rows * Kd * 2, 0x00020000);
-    const int aoff = (lr * Kd + lc) * 2;
-    const int arow64 = 64 * Kd * 2;
-    int br[4];
+    // A rows past the expert's end and B rows past Nout read as zeros (range check)
+    const i32x4 arsrc = buffer_rsrc(A + (int64_t)(row0 + m0) * Kd, (uint32_t)m_rows * Kd * 2);
+    const i32x4 brsrc = buffer_rsrc(B + (int64_t)tl.g * Nrows * Kd, (uint32_t)Nrows * Kd * 2);
+    uint32_t aoff[4], boff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = lr + 64 * i;
-      br[i] = kSwiglu ? (r < 128 ? tl.n_idx * 128 + r : half + tl.n_idx * 128 + (r - 128))
-                      : min(tl.n_idx * BN + r, Nout - 1);
+      const int r = 64 * i + 8 * wv + lrow;
+      aoff[i] = (uint32_t)(r * Kd + lchunk * 8) * 2;
+      int br;
+      if (kSwiglu) br = r < 128 ? tl.n_idx * 128 + r : half + tl.n_idx * 128 + (r - 128);
+      else br = tl.n_idx * BN + r;
+      boff[i] = br < Nrows ? (uint32_t)(br * Kd + lchunk * 8) * 2 : 0x7ffffff0u;
     }
-    const uint16_t* bbase = B + (int64_t)tl.g * Nrows * Kd + lc;
-    const int64_t bo0 = (int64_t)br[0] * Kd, bo1 = (int64_t)br[1] * Kd;
-    const int64_t bo2 = (int64_t)br[2] * Kd, bo3 = (int64_t)br[3] * Kd;
+    const uint32_t ldsw = lds0 + 8 * wv * kRowBytes;
 
-    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-#define A_LD(i, k)                                                                          \
-  ({                                                                                        \
-    auto v_ = __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff + (i) * arow64 + (k) * BK * 2, \
-                                                    0, 0);                                  \
-    *reinterpret_cast<uint4*>(&v_);                                                         \
-  })
-#define G_LD(p) (*reinterpret_cast<const uint4*>(p))
-#define GEMM_GLOAD(k)                                                         \
-  {                                                                           \
-    ra0 = A_LD(0, k); ra1 = A_LD(1, k); ra2 = A_LD(2, k); ra3 = A_LD(3, k);   \
-    const int ko = (k) * BK;                                                  \
-    rb0 = G_LD(bbase + bo0 + ko); rb1 = G_LD(bbase + bo1 + ko);               \
-    rb2 = G_LD(bbase + bo2 + ko); rb3 = G_LD(bbase + bo3 + ko);               \
-  }
-#define GEMM_LSTORE(buf)                                                      \
-  {                                                                           \
-    uint16_t* ad = &As[buf][sA];                                              \
-    uint16_t* bd = &Bs[buf][sA];                                              \
-    *reinterpret_cast<uint4*>(ad) = ra0;                                      \
-    if (m_rows > 64) *reinterpret_cast<uint4*>(ad + 64 * LDA) = ra1;          \
-    if (m_rows > 128) *reinterpret_cast<uint4*>(ad + 128 * LDA) = ra2;        \
-    if (m_rows > 192) *reinterpret_cast<uint4*>(ad + 192 * LDA) = ra3;        \
-    *reinterpret_cast<uint4*>(bd) = rb0;                                      \
-    *reinterpret_cast<uint4*>(bd + 64 * LDA) = rb1;                           \
-    *reinterpret_cast<uint4*>(bd + 128 * LDA) = rb2;                          \
-    *reinterpret_cast<uint4*>(bd + 192 * LDA) = rb3;                          \
+#define STAGE_LOAD(kt, st)                                                            \
+  {                                                                                   \
+    const uint32_t sa_ = ldsw + (st) * sStage;                                        \
+    const uint32_t ko_ = (uint32_t)(kt) * kRowBytes;                                  \
+    load_to_lds(arsrc, sa_, aoff[0] + ko_);                                           \
+    if (nA > 1) load_to_lds(arsrc, sa_ + 64 * kRowBytes, aoff[1] + ko_);              \
+    if (nA > 2) load_to_lds(arsrc, sa_ + 128 * kRowBytes, aoff[2] + ko_);             \
+    if (nA > 3) load_to_lds(arsrc, sa_ + 192 * kRowBytes, aoff[3] + ko_);             \
+    load_to_lds(brsrc, sa_ + sA, boff[0] + ko_);                                      \
+    load_to_lds(brsrc, sa_ + sA + 64 * kRowBytes, boff[1] + ko_);                     \
+    load_to_lds(brsrc, sa_ + sA + 128 * kRowBytes, boff[2] + ko_);                    \
+    load_to_lds(brsrc, sa_ + sA + 192 * kRowBytes, boff[3] + ko_);                    \
   }
 
     f32x16 acc[2][4];
@@ -274,54 +313,52 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
       for (int n = 0; n < 4; ++n)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[mi][n][i] = 0.0f;
-    // B sub-tile rows of this wave: swiglu gate 64wn + 32t, up 128 + 64wn + 32t (t = 0,1);
-    // plain 128wn + 32n
+    // LDS rows read by this lane: A rows 64wm + 32mi + lane%32; B rows per sub-tile n
     int brow[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n)
       brow[n] = (kSwiglu ? ((n & 1) * 128 + 64 * wn + 32 * (n >> 1)) : (128 * wn + 32 * n)) +
                 (lane & 31);
-    const int a_row = 64 * wm + (lane & 31);
+    const int arow0 = 64 * wm + (lane & 31), arow1 = arow0 + 32;
 
-    GEMM_GLOAD(0)
-    GEMM_LSTORE(0)
-    __syncthreads();
+    __syncthreads();  // previous tile's LDS reads are done before the ring is refilled
+    STAGE_LOAD(0, 0)
+    if (nst == 3 && nk > 1) STAGE_LOAD(1, 1)
+    int st = 0;
     for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) {
-        GEMM_GLOAD(kt + 1)
+      // stages issued beyond kt: nst-2 (all but the tail)
+      wait_vm(min(nst - 2, nk - 1 - kt) * per_stage);
+      __syncthreads();
+      if (kt + nst - 1 < nk) {
+        int sn = st + nst - 1;
+        if (sn >= nst) sn -= nst;
+        STAGE_LOAD(kt + nst - 1, sn)
       }
       if (w_on) {
-        const uint16_t* as = As[buf];
-        const uint16_t* bs = Bs[buf];
+        const char* as = smem + st * sStage;
+        const char* bs = as + sA;
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
+          const int c = 2 * s + kq;
           bf16x8 b[4];
 #pragma unroll
           for (int n = 0; n < 4; ++n)
-            b[n] = *reinterpret_cast<const bf16x8*>(bs + brow[n] * LDA + 16 * s + kq);
-          const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(as + a_row * LDA + 16 * s + kq);
+            b[n] = *reinterpret_cast<const bf16x8*>(bs + swz(brow[n], c));
+          const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(as + swz(arow0, c));
 #pragma unroll
           for (int n = 0; n < 4; ++n)
             acc[0][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[n], acc[0][n], 0, 0, 0);
           if (w_sub1) {
-            const bf16x8 a1 =
-                *reinterpret_cast<const bf16x8*>(as + (a_row + 32) * LDA + 16 * s + kq);
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(as + swz(arow1, c));
 #pragma unroll
             for (int n = 0; n < 4; ++n)
               acc[1][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[n], acc[1][n], 0, 0, 0);
           }
         }
       }
-      if (kt + 1 < nk) {
-        GEMM_LSTORE(buf ^ 1)
-      }
-      __syncthreads();
+      if (++st == nst) st = 0;
     }
-#undef A_LD
-#undef G_LD
-#undef GEMM_GLOAD
-#undef GEMM_LSTORE
+#undef STAGE_LOAD
 
     if (w_on) {
 #pragma unroll

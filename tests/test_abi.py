@@ -57,7 +57,7 @@ def prob(L, **kw):
     (dict(E=64, G=2, J=9, M=1), "J="), (dict(K=9), "K="), (dict(K=17, E=64, G=4), "K="),
     (dict(S=2), "S="), (dict(act_dtype=0, expert_dtype=2), "dtypes"),
     (dict(act_dtype=1, expert_dtype=0), "dtypes"), (dict(act_dtype=3, expert_dtype=3), "dtypes"),
-    (dict(T=2 ** 29, K=8), "T*(K+1)"),
+    (dict(T=2 ** 29, K=8), "T*(K+1)"), (dict(H=65536, I=8192), "H*I"),
 ])
 def test_invalid_problem_rejected_everywhere(L, kw, frag):
     p = prob(L, **kw)

@@ -12,9 +12,55 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kXcds = 8;
+
+// Buffer descriptor for raw loads from p: byte offsets at or past `bytes` read as zero
+// without touching memory (per-dword range check, stride 0).
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  i32x4 r;
+  r.x = (int)(uint32_t)a;
+  r.y = (int)((uint32_t)(a >> 32) & 0xffffu);
+  r.z = (int)bytes;
+  r.w = 0x00020000;
+  return r;
+}
+
+// Byte address of a __shared__ object in the workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Buffer loads whose data goes to LDS instead of registers: lane l writes its 16 (or
+// 4) bytes at LDS byte address lds + 16*l (4*l).  `lds` must be wave-uniform.  The
+// compiler does not see these loads: the caller waits for them with wait_vmcnt and
+// a barrier before reading the LDS they fill.
+__device__ __forceinline__ void load16_to_lds(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               ::"s"(lds), "v"(voff), "s"(rsrc) : "memory");
+}
+__device__ __forceinline__ void load4_to_lds(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               ::"s"(lds), "v"(voff), "s"(rsrc) : "memory");
+}
+
+// Wait until at most n (0..15) vector-memory operations of this wave are outstanding;
+// other n wait for all.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define MOE_VMCNT_CASE(k) \
+  case k: __builtin_amdgcn_s_waitcnt(0x0F70 | k); break;
+    MOE_VMCNT_CASE(1) MOE_VMCNT_CASE(2) MOE_VMCNT_CASE(3) MOE_VMCNT_CASE(4)
+    MOE_VMCNT_CASE(5) MOE_VMCNT_CASE(6) MOE_VMCNT_CASE(7) MOE_VMCNT_CASE(8)
+    MOE_VMCNT_CASE(9) MOE_VMCNT_CASE(10) MOE_VMCNT_CASE(11) MOE_VMCNT_CASE(12)
+    MOE_VMCNT_CASE(13) MOE_VMCNT_CASE(14) MOE_VMCNT_CASE(15)
+#undef MOE_VMCNT_CASE
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

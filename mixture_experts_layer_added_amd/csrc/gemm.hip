@@ -190,41 +190,10 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
 // column (l%32), the same k of B; result element i of lane l is row
 // 8*(i/4) + 4*(l/32) + i%4, column l%32.
 // ---------------------------------------------------------------------------
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kRowBytes = BK * 2;               // one row of one stage: a full 128-B line
 constexpr int kBStage = BN * kRowBytes;         // 32 KiB
 constexpr int kRing = 3 * (128 * kRowBytes + kBStage);  // 144 KiB
-
-__device__ __forceinline__ i32x4 buffer_rsrc(const void* p, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  i32x4 r;
-  r.x = (int)(uint32_t)a;
-  r.y = (int)((uint32_t)(a >> 32) & 0xffffu);
-  r.z = (int)bytes;
-  r.w = 0x00020000;
-  return r;
-}
-
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// 16 bytes per lane from buffer offset voff into LDS at lds + 16*lane.
-__device__ __forceinline__ void load_to_lds(i32x4 rsrc, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               ::"s"(lds), "v"(voff), "s"(rsrc) : "memory");
-}
-
-// Wait until at most n vector-memory operations of this wave are outstanding.
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-  }
-}
 
 // byte offset of (row, 16-byte k-chunk c) inside an operand stage: rows of 128 B,
 // chunk slots xor-swizzled by (row >> 1) & 7 so 16 consecutive rows at one chunk hit
@@ -296,14 +265,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
   {                                                                                   \
     const uint32_t sa_ = ldsw + (st) * sStage;                                        \
     const uint32_t ko_ = (uint32_t)(kt) * kRowBytes;                                  \
-    load_to_lds(arsrc, sa_, aoff[0] + ko_);                                           \
-    if (nA > 1) load_to_lds(arsrc, sa_ + 64 * kRowBytes, aoff[1] + ko_);              \
-    if (nA > 2) load_to_lds(arsrc, sa_ + 128 * kRowBytes, aoff[2] + ko_);             \
-    if (nA > 3) load_to_lds(arsrc, sa_ + 192 * kRowBytes, aoff[3] + ko_);             \
-    load_to_lds(brsrc, sa_ + sA, boff[0] + ko_);                                      \
-    load_to_lds(brsrc, sa_ + sA + 64 * kRowBytes, boff[1] + ko_);                     \
-    load_to_lds(brsrc, sa_ + sA + 128 * kRowBytes, boff[2] + ko_);                    \
-    load_to_lds(brsrc, sa_ + sA + 192 * kRowBytes, boff[3] + ko_);                    \
+    load16_to_lds(arsrc, sa_, aoff[0] + ko_);                                           \
+    if (nA > 1) load16_to_lds(arsrc, sa_ + 64 * kRowBytes, aoff[1] + ko_);              \
+    if (nA > 2) load16_to_lds(arsrc, sa_ + 128 * kRowBytes, aoff[2] + ko_);             \
+    if (nA > 3) load16_to_lds(arsrc, sa_ + 192 * kRowBytes, aoff[3] + ko_);             \
+    load16_to_lds(brsrc, sa_ + sA, boff[0] + ko_);                                      \
+    load16_to_lds(brsrc, sa_ + sA + 64 * kRowBytes, boff[1] + ko_);                     \
+    load16_to_lds(brsrc, sa_ + sA + 128 * kRowBytes, boff[2] + ko_);                    \
+    load16_to_lds(brsrc, sa_ + sA + 192 * kRowBytes, boff[3] + ko_);                    \
   }
 
     f32x16 acc[2][4];
@@ -327,7 +296,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
     int st = 0;
     for (int kt = 0; kt < nk; ++kt) {
       // stages issued beyond kt: nst-2 (all but the tail)
-      wait_vm(min(nst - 2, nk - 1 - kt) * per_stage);
+      wait_vmcnt(min(nst - 2, nk - 1 - kt) * per_stage);
       __syncthreads();
       if (kt + nst - 1 < nk) {
         int sn = st + nst - 1;

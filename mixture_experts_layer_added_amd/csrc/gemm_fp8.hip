@@ -11,13 +11,20 @@
 // the instruction's scale operands), and the partial is promoted into the fp32
 // accumulator as acc += partial * (s_a * s_w).
 //
-// Tile: 64 rows x BN weight rows, 64-deep k steps double-buffered in LDS, four waves
-// side by side along N, each wave 2 (rows) x NSUB (columns) MFMA tiles of 32x32.
-//   up   (kSwiglu, NSUB=2): BN = 256 = 128 gate rows + the matching 128 up rows; each
-//        wave holds gate and up of the same h element, applies SwiGLU, and the tile's
-//        128 h columns are exactly one quantisation tile of h: amax per row across the
-//        four waves, scale = amax/448, RNE-saturating E4M3 codes.
-//   down (NSUB=1): BN = 128 output columns, bf16 output.
+// Tile: 256 rows (one tile holds all rows of an expert, so its weights stream from
+// HBM once) x 256 weight rows x one 128-deep scale block per k step; a row of a step
+// is one full 128-byte line.  Operands and the activation scales of a step go from
+// memory straight into LDS (buffer loads with the LDS destination bit); the ring holds
+// three steps when the A stage (ceil(rows/64)*64 rows) is at most 128 rows, else two.
+// Activation rows past the expert's end arrive as zeros (range-checked descriptor).
+// Eight waves, wave w owns rows 32w..32w+31 and all 256 columns (8 MFMA tiles of
+// 32x32); waves past the expert's rows skip their MFMAs.
+//   up   (kSwiglu): the 256 weight rows are 128 gate rows + the matching 128 up rows;
+//        tile n even is gate, n+1 the matching up, so each lane holds gate and up of
+//        the same h element.  The tile's 128 h columns are one quantisation tile of h
+//        and lie in one wave: per-row amax by lane shuffles, scale = amax/448,
+//        RNE-saturating E4M3 codes.
+//   down: 256 output columns, bf16 output.
 // Operand layout (32x32x64 f8): lane l supplies row l%32 and k = 32*(l/32)..+31 of A,
 // column l%32 and the same k of B; result element i of lane l is row
 // 8*(i/4) + 4*(l/32) + i%4, column l%32.
@@ -28,7 +35,9 @@ namespace {
 
 constexpr int kMaxGroups = 513;
 constexpr int kSchedPer = 9;
-constexpr int FBM = 64, FBK = 64, FLD = FBK + 16;  // LDS row stride in bytes
+constexpr int FBM = 256, FBN = 256, FBK = 128;   // FBK bytes = one 128-B line per row
+constexpr int kFB = FBN * FBK;                    // B stage: 32 KiB
+constexpr int kFRing = 3 * (128 * FBK + kFB);     // 144 KiB
 
 __device__ __forceinline__ void fp8_schedule(const int32_t* __restrict__ offsets, int NG, int BM,
                                              int* s_mt) {
@@ -62,223 +71,222 @@ __device__ __forceinline__ void fp8_schedule(const int32_t* __restrict__ offsets
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
-template <bool kSwiglu, int NSUB>
-__global__ __launch_bounds__(256, 2) void k_gemm_fp8(
+// byte offset of (row, 16-byte chunk c) inside an operand stage: 128-B rows, chunk
+// slots xor-swizzled by (row >> 1) & 7 (16 consecutive rows at one chunk hit 16
+// distinct bank groups)
+__device__ __forceinline__ int fswz(int r, int c) { return r * FBK + ((c ^ (r >> 1)) & 7) * 16; }
+
+__device__ __forceinline__ i32x8 frag32(const char* p0, const char* p1) {
+  const uint4 u0 = *reinterpret_cast<const uint4*>(p0);
+  const uint4 u1 = *reinterpret_cast<const uint4*>(p1);
+  i32x8 f;
+  f[0] = u0.x; f[1] = u0.y; f[2] = u0.z; f[3] = u0.w;
+  f[4] = u1.x; f[5] = u1.y; f[6] = u1.z; f[7] = u1.w;
+  return f;
+}
+
+template <bool kSwiglu>
+__global__ __launch_bounds__(512, 1) void k_gemm_fp8(
     const uint8_t* __restrict__ A, const float* __restrict__ A_scale,
     const uint8_t* __restrict__ B, const float* __restrict__ B_scale, void* __restrict__ C,
     float* __restrict__ C_scale, const int32_t* __restrict__ offsets, int NG, int Kd, int Nrows,
     int Nout, int half) {
-  constexpr int BN = 128 * NSUB;
-  constexpr int BCH = BN * FBK / 16 / 256;  // 16-byte B chunks per thread per k step
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][FBM * FLD];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * FLD];
-  __shared__ float s_sa[2][FBM];
-  __shared__ float s_red[4][FBM];
+  __shared__ __attribute__((aligned(1024))) char smem[kFRing];
+  __shared__ __attribute__((aligned(16))) float s_sa[3][FBM];
   __shared__ int mt_start[kMaxGroups + 1];
   fp8_schedule(offsets, NG, FBM, mt_start);
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int nt = kSwiglu ? half / 128 : Nout / 128;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nt = kSwiglu ? half / 128 : (Nout + FBN - 1) / FBN;
   const int ntiles = mt_start[NG] * nt;
-  const int nkb = Kd / 128;   // scale blocks along k
-  const int nk = Kd / FBK;    // k steps
-  const int nbr = Nrows / 128;
+  const int nk = Kd / FBK;     // k steps = scale blocks along k
+  const int nbr = Nrows / 128;  // weight-scale block rows
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
+  const uint32_t lds_sa = __builtin_amdgcn_readfirstlane(lds_offset(&s_sa[0][0]));
+  // loader: instruction i of wave wv fills rows 64i + 8wv .. +7 of an operand stage;
+  // lane l writes row 64i + 8wv + (l>>3), slot l&7 = k-chunk (l&7) ^ ((row>>1)&7)
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ ((4 * (wv & 1) + (lane >> 4)) & 7);
+  const int kq = lane >> 5;
 
   const int P = gridDim.x, per_xcd = P / kXcds;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int chunk = (ntiles + kXcds - 1) / kXcds;
   const int end = min(ntiles, (xcd + 1) * chunk);
   for (int tile = xcd * chunk + slot; tile < end; tile += per_xcd) {
-    // decode (group, column tile, row tile)
+    // decode (group, column tile); one row tile per 256 rows of a group
     int lo = 0, hi = NG;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (mt_start[mid] * nt <= tile) lo = mid;
       else hi = mid;
     }
-    const int g = lo;
+    const int g = __builtin_amdgcn_readfirstlane(lo);
     const int mt = mt_start[g + 1] - mt_start[g];
     const int local = tile - mt_start[g] * nt;
-    const int n_idx = local / mt, m_idx = local % mt;
+    const int n_idx = __builtin_amdgcn_readfirstlane(local / mt);
+    const int m_idx = __builtin_amdgcn_readfirstlane(local % mt);
     const int row0 = offsets[g];
     const int m_g = offsets[g + 1] - row0;
     const int m0 = m_idx * FBM;
+    const int m_rows = min(FBM, m_g - m0);
+    const bool w_on = 32 * wv < m_rows;
+    const int nA = (m_rows + 63) >> 6;
+    const int sA = nA * 64 * FBK;
+    const int sStage = sA + kFB;
+    const int nst = (3 * sStage <= kFRing) ? 3 : 2;
+    const bool ld_sa = wv < nA;  // waves 0..nA-1 bring 64 activation scales each
+    const int per_stage = nA + 4 + (ld_sa ? 1 : 0);
 
-    // loaders: A one 16-byte chunk per thread (row tid/4), B BCH chunks
-    const int arow = tid >> 2, akc = (tid & 3) * 16;
-    const int64_t a_off = (int64_t)(row0 + min(m0 + arow, m_g - 1)) * Kd + akc;
-    // B chunk i of this thread: row tid/4 + 64*i, the same 16 bytes of k as A
-    auto brow_of = [&](int r) {
-      if (kSwiglu) return r < 128 ? n_idx * 128 + r : half + n_idx * 128 + (r - 128);
-      return n_idx * 128 + r;
-    };
-    const int64_t bg = (int64_t)g * Nrows;
-    const int64_t b_off0 = (bg + brow_of(arow)) * Kd + akc;
-    const int64_t b_off1 = (bg + brow_of(arow + 64)) * Kd + akc;
-    const int64_t b_off2 = BCH > 2 ? (bg + brow_of(arow + 128)) * Kd + akc : 0;
-    const int64_t b_off3 = BCH > 2 ? (bg + brow_of(arow + 192)) * Kd + akc : 0;
-    const int64_t sa_row = (int64_t)(row0 + min(m0 + (tid & 63), m_g - 1)) * nkb;
-    // weight-scale block rows of this wave's column tiles
-    const int wblk0 = n_idx;                              // gate rows / output columns
-    const int wblk1 = kSwiglu ? half / 128 + n_idx : n_idx;  // up rows
-    const float* bsc = B_scale + (int64_t)g * nbr * nkb;
+    const i32x4 arsrc = buffer_rsrc(A + (int64_t)(row0 + m0) * Kd, (uint32_t)m_rows * Kd);
+    const i32x4 brsrc = buffer_rsrc(B + (int64_t)g * Nrows * Kd, (uint32_t)Nrows * Kd);
+    const i32x4 srsrc = buffer_rsrc(A_scale + (int64_t)(row0 + m0) * nk, (uint32_t)m_rows * nk * 4);
+    uint32_t aoff[4], boff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 64 * i + 8 * wv + lrow;
+      aoff[i] = (uint32_t)(r * Kd + lchunk * 16);
+      int br;
+      if (kSwiglu) br = r < 128 ? n_idx * 128 + r : half + n_idx * 128 + (r - 128);
+      else br = n_idx * FBN + r;
+      boff[i] = br < Nrows ? (uint32_t)(br * Kd + lchunk * 16) : 0x7ffffff0u;
+    }
+    const uint32_t soff = (uint32_t)((64 * wv + lane) * nk) * 4;
+    const uint32_t ldsw = lds0 + 8 * wv * FBK;
+    const uint32_t ldss = lds_sa + 64 * wv * 4;
+    // weight-scale block rows: up: gate block n_idx (tiles n even), up block
+    // half/128 + n_idx (n odd); down: blocks 2 n_idx (n < 4) and 2 n_idx + 1 (n >= 4)
+    const float* bsc = B_scale + (int64_t)g * nbr * nk;
+    const int wb0 = kSwiglu ? n_idx : min(2 * n_idx, nbr - 1);
+    const int wb1 = kSwiglu ? half / 128 + n_idx : min(2 * n_idx + 1, nbr - 1);
 
-    uint4 ra, rb0, rb1, rb2, rb3;
-    float rsa = 0.0f;
-#define FP8_GLOAD(kt_)                                                                        \
-  {                                                                                           \
-    ra = *reinterpret_cast<const uint4*>(A + a_off + (kt_) * FBK);                            \
-    rb0 = *reinterpret_cast<const uint4*>(B + b_off0 + (kt_) * FBK);                          \
-    rb1 = *reinterpret_cast<const uint4*>(B + b_off1 + (kt_) * FBK);                          \
-    if (BCH > 2) {                                                                            \
-      rb2 = *reinterpret_cast<const uint4*>(B + b_off2 + (kt_) * FBK);                        \
-      rb3 = *reinterpret_cast<const uint4*>(B + b_off3 + (kt_) * FBK);                        \
-    }                                                                                         \
-    if ((((kt_) & 1) == 0) && tid < FBM) rsa = A_scale[sa_row + ((kt_) >> 1)];                \
+#define FSTAGE_LOAD(kt, st)                                                           \
+  {                                                                                   \
+    const uint32_t sa_ = ldsw + (st) * sStage;                                        \
+    const uint32_t ko_ = (uint32_t)(kt) * FBK;                                        \
+    load16_to_lds(arsrc, sa_, aoff[0] + ko_);                                         \
+    if (nA > 1) load16_to_lds(arsrc, sa_ + 64 * FBK, aoff[1] + ko_);                  \
+    if (nA > 2) load16_to_lds(arsrc, sa_ + 128 * FBK, aoff[2] + ko_);                 \
+    if (nA > 3) load16_to_lds(arsrc, sa_ + 192 * FBK, aoff[3] + ko_);                 \
+    load16_to_lds(brsrc, sa_ + sA, boff[0] + ko_);                                    \
+    load16_to_lds(brsrc, sa_ + sA + 64 * FBK, boff[1] + ko_);                         \
+    load16_to_lds(brsrc, sa_ + sA + 128 * FBK, boff[2] + ko_);                        \
+    load16_to_lds(brsrc, sa_ + sA + 192 * FBK, boff[3] + ko_);                        \
+    if (ld_sa) load4_to_lds(srsrc, ldss + (st) * (FBM * 4), soff + (uint32_t)(kt) * 4); \
   }
-#define FP8_LSTORE(kt_, buf_)                                                                 \
-  {                                                                                           \
-    *reinterpret_cast<uint4*>(&As[buf_][arow * FLD + akc]) = ra;                              \
-    *reinterpret_cast<uint4*>(&Bs[buf_][(tid >> 2) * FLD + akc]) = rb0;                       \
-    *reinterpret_cast<uint4*>(&Bs[buf_][((tid >> 2) + 64) * FLD + akc]) = rb1;                \
-    if (BCH > 2) {                                                                            \
-      *reinterpret_cast<uint4*>(&Bs[buf_][((tid >> 2) + 128) * FLD + akc]) = rb2;             \
-      *reinterpret_cast<uint4*>(&Bs[buf_][((tid >> 2) + 192) * FLD + akc]) = rb3;             \
-    }                                                                                         \
-    if ((((kt_) & 1) == 0) && tid < FBM) s_sa[((kt_) >> 1) & 1][tid] = rsa;                   \
-  }
 
-    f32x16 acc[2][NSUB], tmp[2][NSUB];
+    f32x16 acc[8];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int n = 0; n < 8; ++n)
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mi][s][i] = 0.0f;
+      for (int i = 0; i < 16; ++i) acc[n][i] = 0.0f;
+    const int arow = 32 * wv + (lane & 31);
 
-    const int kq = (lane >> 5) * 32;
-    FP8_GLOAD(0)
-    FP8_LSTORE(0, 0)
-    __syncthreads();
+    __syncthreads();  // previous tile's LDS reads are done before the ring is refilled
+    FSTAGE_LOAD(0, 0)
+    if (nst == 3 && nk > 1) FSTAGE_LOAD(1, 1)
+    int st = 0;
     for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) FP8_GLOAD(kt + 1)
-      i32x8 af[2], bfr[NSUB];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const uint8_t* p = &As[buf][(32 * mi + (lane & 31)) * FLD + kq];
-        const uint4 u0 = *reinterpret_cast<const uint4*>(p);
-        const uint4 u1 = *reinterpret_cast<const uint4*>(p + 16);
-        af[mi][0] = u0.x; af[mi][1] = u0.y; af[mi][2] = u0.z; af[mi][3] = u0.w;
-        af[mi][4] = u1.x; af[mi][5] = u1.y; af[mi][6] = u1.z; af[mi][7] = u1.w;
+      const float sw0 = bsc[(int64_t)wb0 * nk + kt];
+      const float sw1 = bsc[(int64_t)wb1 * nk + kt];
+      wait_vmcnt(min(nst - 2, nk - 1 - kt) * per_stage);
+      __syncthreads();
+      if (kt + nst - 1 < nk) {
+        int sn = st + nst - 1;
+        if (sn >= nst) sn -= nst;
+        FSTAGE_LOAD(kt + nst - 1, sn)
       }
+      if (w_on) {
+        const char* as = smem + st * sStage;
+        const char* bs = as + sA;
+        // A fragments of both 64-deep halves: chunks 2*kq, 2*kq+1 and 4 + the same
+        const i32x8 a0 = frag32(as + fswz(arow, 2 * kq), as + fswz(arow, 2 * kq + 1));
+        const i32x8 a1 = frag32(as + fswz(arow, 4 + 2 * kq), as + fswz(arow, 5 + 2 * kq));
+        float sa[16];
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        const uint8_t* p = &Bs[buf][(32 * wv + 128 * s + (lane & 31)) * FLD + kq];
-        const uint4 u0 = *reinterpret_cast<const uint4*>(p);
-        const uint4 u1 = *reinterpret_cast<const uint4*>(p + 16);
-        bfr[s][0] = u0.x; bfr[s][1] = u0.y; bfr[s][2] = u0.z; bfr[s][3] = u0.w;
-        bfr[s][4] = u1.x; bfr[s][5] = u1.y; bfr[s][6] = u1.z; bfr[s][7] = u1.w;
-      }
-      const bool first_half = (kt & 1) == 0;
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *reinterpret_cast<const float4*>(&s_sa[st][32 * wv + 8 * q + 4 * kq]);
+          sa[4 * q + 0] = v.x; sa[4 * q + 1] = v.y; sa[4 * q + 2] = v.z; sa[4 * q + 3] = v.w;
+        }
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+        for (int n = 0; n < 8; n += 2) {
+          f32x16 t[2];
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-          if (first_half) {
+          for (int u = 0; u < 2; ++u) {
+            const int nn = n + u;
+            const int brow = (kSwiglu ? ((nn & 1) * 128 + 32 * (nn >> 1)) : 32 * nn) + (lane & 31);
+            const i32x8 b0 = frag32(bs + fswz(brow, 2 * kq), bs + fswz(brow, 2 * kq + 1));
             f32x16 z;
 #pragma unroll
             for (int i = 0; i < 16; ++i) z[i] = 0.0f;
-            tmp[mi][s] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[s], z, 0, 0, 0,
-                                                                         127, 0, 127);
-          } else {
-            tmp[mi][s] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bfr[s], tmp[mi][s],
-                                                                         0, 0, 0, 127, 0, 127);
+            t[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, z, 0, 0, 0, 127, 0, 127);
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int nn = n + u;
+            const int brow = (kSwiglu ? ((nn & 1) * 128 + 32 * (nn >> 1)) : 32 * nn) + (lane & 31);
+            const i32x8 b1 = frag32(bs + fswz(brow, 4 + 2 * kq), bs + fswz(brow, 5 + 2 * kq));
+            t[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, t[u], 0, 0, 0, 127, 0,
+                                                                    127);
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int nn = n + u;
+            const float sw = kSwiglu ? ((nn & 1) ? sw1 : sw0) : (nn < 4 ? sw0 : sw1);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              acc[nn][i] = __builtin_fmaf(t[u][i], sa[i] * sw, acc[nn][i]);
           }
         }
-      if (!first_half) {
-        // promote the finished 128-deep block: acc += partial * (s_a[row] * s_w)
-        const int kb = kt >> 1;
-        float sw[NSUB];
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) sw[s] = bsc[(int64_t)(s == 0 ? wblk0 : wblk1) * nkb + kb];
-        const float* sa = s_sa[kb & 1];
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 a4 = *reinterpret_cast<const float4*>(&sa[32 * mi + 8 * q + 4 * (lane >> 5)]);
-            const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-              for (int s = 0; s < NSUB; ++s)
-                acc[mi][s][4 * q + j] =
-                    __builtin_fmaf(tmp[mi][s][4 * q + j], av[j] * sw[s], acc[mi][s][4 * q + j]);
-          }
       }
-      if (kt + 1 < nk) FP8_LSTORE(kt + 1, buf ^ 1)
-      __syncthreads();
+      if (++st == nst) st = 0;
     }
-#undef FP8_GLOAD
-#undef FP8_LSTORE
+#undef FSTAGE_LOAD
 
+    if (!w_on) continue;
     if constexpr (kSwiglu) {
-      // h = silu(gate) * up; per-row amax over the tile's 128 columns (4 waves x 32)
-      float hv[2][16];
-      float rmax[2][16];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          hv[mi][i] = silu(acc[mi][0][i]) * acc[mi][1][i];
-          float m = __builtin_fabsf(hv[mi][i]);
-#pragma unroll
-          for (int off = 1; off < 32; off <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
-          rmax[mi][i] = m;
-        }
-      if ((lane & 31) == 0)
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            s_red[wv][32 * mi + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)] = rmax[mi][i];
-      __syncthreads();
+      // h = silu(gate) * up; the row's 128 h columns are the 4 gate/up pairs x 32 lanes
+      float hv[4][16];
       uint8_t* hq = static_cast<uint8_t*>(C);
       const int ncb = Nout / 128;
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int i = 0; i < 16; ++i) {
+        float m = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = 32 * mi + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          const float amax = __builtin_fmaxf(__builtin_fmaxf(s_red[0][r], s_red[1][r]),
-                                             __builtin_fmaxf(s_red[2][r], s_red[3][r]));
-          const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
-          const int m = m0 + r;
-          if (m < m_g) {
-            hq[(int64_t)(row0 + m) * Nout + n_idx * 128 + 32 * wv + (lane & 31)] =
-                static_cast<uint8_t>(f32_to_e4m3_bits(hv[mi][i] / sc));
-            if (wv == 0 && (lane & 31) == 0) C_scale[(int64_t)(row0 + m) * ncb + n_idx] = sc;
-          }
+        for (int t = 0; t < 4; ++t) {
+          hv[t][i] = silu(acc[2 * t][i]) * acc[2 * t + 1][i];
+          m = __builtin_fmaxf(m, __builtin_fabsf(hv[t][i]));
         }
-      __syncthreads();  // s_red is reused by the next tile
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+        const float sc = m > 0.0f ? m / 448.0f : 1.0f;
+        const int r = 32 * wv + 8 * (i >> 2) + 4 * kq + (i & 3);
+        if (r < m_rows) {
+          uint8_t* hp = hq + (int64_t)(row0 + m0 + r) * Nout + n_idx * 128 + (lane & 31);
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            hp[32 * t] = static_cast<uint8_t>(f32_to_e4m3_bits(hv[t][i] / sc));
+          if ((lane & 31) == 0) C_scale[(int64_t)(row0 + m0 + r) * ncb + n_idx] = sc;
+        }
+      }
     } else {
       uint16_t* y = static_cast<uint16_t*>(C);
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int i = 0; i < 16; ++i) {
+        const int r = 32 * wv + 8 * (i >> 2) + 4 * kq + (i & 3);
+        if (r >= m_rows) continue;
+        uint16_t* yp = y + (int64_t)(row0 + m0 + r) * Nout + n_idx * FBN + (lane & 31);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = m0 + 32 * mi + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          if (m < m_g)
-            y[(int64_t)(row0 + m) * Nout + n_idx * 128 + 32 * wv + (lane & 31)] =
-                f32_to_bf16_bits(acc[mi][0][i]);
-        }
+        for (int n = 0; n < 8; ++n)
+          if (n_idx * FBN + 32 * n < Nout) yp[32 * n] = f32_to_bf16_bits(acc[n][i]);
+      }
     }
   }
 }
 
 int fp8_grid(int cus) {
-  const int p = (cus * 2 / kXcds) * kXcds;
+  const int p = (cus / kXcds) * kXcds;
   return p < kXcds ? kXcds : p;
 }
 
@@ -287,7 +295,7 @@ int fp8_grid(int cus) {
 hipError_t launch_fp8_up(const Dims& d, const void* xs, const float* xs_scale,
                          const int32_t* offsets, const void* w13, const float* w13_scale, void* h,
                          float* h_scale, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemm_fp8<true, 2>), dim3(fp8_grid(device_cu_count())), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_gemm_fp8<true>), dim3(fp8_grid(device_cu_count())), dim3(512), 0, st,
                      static_cast<const uint8_t*>(xs), xs_scale, static_cast<const uint8_t*>(w13),
                      w13_scale, h, h_scale, offsets, d.E + d.S, d.H, 2 * d.I, d.I, d.I);
   return hipGetLastError();
@@ -296,7 +304,7 @@ hipError_t launch_fp8_up(const Dims& d, const void* xs, const float* xs_scale,
 hipError_t launch_fp8_down(const Dims& d, const void* h, const float* h_scale,
                            const int32_t* offsets, const void* w2, const float* w2_scale, void* ys,
                            hipStream_t st) {
-  hipLaunchKernelGGL((k_gemm_fp8<false, 1>), dim3(fp8_grid(device_cu_count())), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_gemm_fp8<false>), dim3(fp8_grid(device_cu_count())), dim3(512), 0, st,
                      static_cast<const uint8_t*>(h), h_scale, static_cast<const uint8_t*>(w2),
                      w2_scale, ys, nullptr, offsets, d.E + d.S, d.I, d.H, d.H, 0);
   return hipGetLastError();

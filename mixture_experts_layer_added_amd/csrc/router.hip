@@ -20,36 +20,37 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Logits: a 32-token x 64-expert tile per 128-thread workgroup (two workgroups per CU
-// at T=4096), each thread a 4x4 register tile.  Hidden chunks of 32 go through LDS
-// transposed ([h][token] and [h][expert]) so one 16-byte LDS read gives a thread its
-// 4 tokens (or 4 experts) at one h; the reads for h+1 are issued before the 16 fused
-// multiply-adds of h so LDS latency hides behind them.  Every accumulator sees h in
-// increasing order.
+// Logits: lanes are tokens, experts are wave-uniform.  A workgroup takes 64 tokens x
+// 32 experts; its 8 waves share the tokens' hidden chunk (64 h at a time, in LDS as
+// fp32, one padded row per token) and each wave owns 4 experts, whose router-weight
+// rows it reads with scalar loads, so each fused multiply-add takes its weight operand
+// from a scalar register and its x operand from the lane's own row.  Every
+// accumulator sees h in increasing order.
 // ---------------------------------------------------------------------------
-constexpr int LT = 32, LE = 64, LH = 32, LTHREADS = 128;
+constexpr int RT = 64, RE = 4, RWV = 8, RH = 64, RROW = RH + 4;
 
 template <typename XT>
-__global__ __launch_bounds__(LTHREADS) void k_router_logits(const XT* __restrict__ x,
-                                                            const float* __restrict__ w,
-                                                            float* __restrict__ z,
-                                                            int32_t* __restrict__ counts, int T,
-                                                            int H, int E) {
-  __shared__ __attribute__((aligned(16))) float xs[2][LH][LT];
-  __shared__ __attribute__((aligned(16))) float wsm[2][LH][LE];
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * LT, e0 = blockIdx.y * LE;
+__global__ __launch_bounds__(RWV * kWave) void k_router_logits(const XT* __restrict__ x,
+                                                               const float* __restrict__ w,
+                                                               float* __restrict__ z,
+                                                               int32_t* __restrict__ counts,
+                                                               int T, int H, int E) {
+  __shared__ __attribute__((aligned(16))) float xs[2][RT * RROW];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = blockIdx.x * RT;
+  const int eb = blockIdx.y * (RE * RWV) + wv * RE;
   if (blockIdx.x == 0 && blockIdx.y == 0)
-    for (int e = tid; e < E; e += LTHREADS) counts[e] = 0;  // zeroed before the select kernel
+    for (int e = tid; e < E; e += RWV * kWave) counts[e] = 0;  // zeroed before the select kernel
 
-  // loaders: x 32 rows x 32 h (4 threads per row, 8 h each); w 64 rows x 32 h
-  // (2 threads per row, 16 h each)
-  const int xrow = tid >> 2, xh = (tid & 3) * 8;
-  const int wrow = tid >> 1, wh = (tid & 1) * 16;
-  const XT* xp = x + (int64_t)min(t0 + xrow, T - 1) * H + xh;
-  const float* wp = w + (int64_t)min(e0 + wrow, E - 1) * H + wh;
+  // loader: token row tid/8, 8 consecutive h at (tid%8)*8
+  const int lr = tid >> 3, lh = (tid & 7) * 8;
+  const XT* xp = x + (int64_t)min(t0 + lr, T - 1) * H + lh;
+  const float* wr[RE];
+#pragma unroll
+  for (int e = 0; e < RE; ++e) wr[e] = w + (int64_t)min(eb + e, E - 1) * H;
 
-  float xr[8], wr[16];
+  float xr[8];
   auto gload = [&](int h0) {
     if constexpr (sizeof(XT) == 2) {
       const uint4 v = *reinterpret_cast<const uint4*>(xp + h0);
@@ -65,61 +66,73 @@ __global__ __launch_bounds__(LTHREADS) void k_router_logits(const XT* __restrict
       xr[0] = a.x; xr[1] = a.y; xr[2] = a.z; xr[3] = a.w;
       xr[4] = b.x; xr[5] = b.y; xr[6] = b.z; xr[7] = b.w;
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 a = *reinterpret_cast<const float4*>(wp + h0 + 4 * q);
-      wr[4 * q] = a.x; wr[4 * q + 1] = a.y; wr[4 * q + 2] = a.z; wr[4 * q + 3] = a.w;
-    }
   };
   auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xs[buf][xh + i][xrow] = xr[i];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) wsm[buf][wh + i][wrow] = wr[i];
+    float* d = &xs[buf][lr * RROW + lh];
+    *reinterpret_cast<float4*>(d) = make_float4(xr[0], xr[1], xr[2], xr[3]);
+    *reinterpret_cast<float4*>(d + 4) = make_float4(xr[4], xr[5], xr[6], xr[7]);
   };
 
-  const int ty = tid >> 4, tx = tid & 15;  // tokens ty*4.., experts tx*4..
-  float acc[4][4];
+  float acc[RE];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-
-  const int nchunk = H / LH;
+  for (int e = 0; e < RE; ++e) acc[e] = 0.0f;
+  const int nchunk = H / RH;
   gload(0);
   lstore(0);
   __syncthreads();
   for (int c = 0; c < nchunk; ++c) {
     const int buf = c & 1;
-    if (c + 1 < nchunk) gload((c + 1) * LH);
-    float4 xv = *reinterpret_cast<const float4*>(&xs[buf][0][ty * 4]);
-    float4 wv = *reinterpret_cast<const float4*>(&wsm[buf][0][tx * 4]);
-#pragma unroll 8
-    for (int hh = 0; hh < LH; ++hh) {
-      const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
-      const float wa[4] = {wv.x, wv.y, wv.z, wv.w};
-      if (hh + 1 < LH) {
-        xv = *reinterpret_cast<const float4*>(&xs[buf][hh + 1][ty * 4]);
-        wv = *reinterpret_cast<const float4*>(&wsm[buf][hh + 1][tx * 4]);
+    if (c + 1 < nchunk) gload((c + 1) * RH);
+    const float* xrow = &xs[buf][lane * RROW];
+    const int hc = c * RH;
+    // register double buffer: the loads of step hh+8 (x from LDS, weights with scalar
+    // loads) are issued before the multiply-adds of step hh, which use the values
+    // loaded one step earlier
+    float xc[8], wc[RE][8];
+    {
+      const float4 xa = *reinterpret_cast<const float4*>(xrow);
+      const float4 xb = *reinterpret_cast<const float4*>(xrow + 4);
+      xc[0] = xa.x; xc[1] = xa.y; xc[2] = xa.z; xc[3] = xa.w;
+      xc[4] = xb.x; xc[5] = xb.y; xc[6] = xb.z; xc[7] = xb.w;
+#pragma unroll
+      for (int e = 0; e < RE; ++e)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wc[e][j] = wr[e][hc + j];
+    }
+#pragma unroll
+    for (int hh = 0; hh < RH; hh += 8) {
+      float xn[8], wn[RE][8];
+      if (hh + 8 < RH) {
+        const float4 xa = *reinterpret_cast<const float4*>(xrow + hh + 8);
+        const float4 xb = *reinterpret_cast<const float4*>(xrow + hh + 12);
+        xn[0] = xa.x; xn[1] = xa.y; xn[2] = xa.z; xn[3] = xa.w;
+        xn[4] = xb.x; xn[5] = xb.y; xn[6] = xb.z; xn[7] = xb.w;
+#pragma unroll
+        for (int e = 0; e < RE; ++e)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) wn[e][j] = wr[e][hc + hh + 8 + j];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(xa[i], wa[j], acc[i][j]);
+        for (int e = 0; e < RE; ++e) acc[e] = __builtin_fmaf(xc[j], wc[e][j], acc[e]);
+      if (hh + 8 < RH) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          xc[j] = xn[j];
+#pragma unroll
+          for (int e = 0; e < RE; ++e) wc[e][j] = wn[e][j];
+        }
+      }
     }
     if (c + 1 < nchunk) lstore(buf ^ 1);
     __syncthreads();
   }
+  const int t = t0 + lane;
+  if (t < T)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= T) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e < E) z[(int64_t)t * E + e] = acc[i][j];
-    }
-  }
+    for (int e = 0; e < RE; ++e)
+      if (eb + e < E) z[(int64_t)t * E + eb + e] = acc[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -289,12 +302,12 @@ hipError_t launch_route(const Dims& d, const void* x, const float* w_router, con
                         int32_t* idx, float* gate, int32_t* counts, float* logits,
                         hipStream_t st) {
   const int T = static_cast<int>(d.T);
-  dim3 g1((T + LT - 1) / LT, (d.E + LE - 1) / LE);
+  dim3 g1((T + RT - 1) / RT, (d.E + RE * RWV - 1) / (RE * RWV));
   if (d.act == MOE_BF16)
-    hipLaunchKernelGGL(k_router_logits<uint16_t>, g1, dim3(LTHREADS), 0, st,
+    hipLaunchKernelGGL(k_router_logits<uint16_t>, g1, dim3(RWV * kWave), 0, st,
                        static_cast<const uint16_t*>(x), w_router, logits, counts, T, d.H, d.E);
   else
-    hipLaunchKernelGGL(k_router_logits<float>, g1, dim3(LTHREADS), 0, st,
+    hipLaunchKernelGGL(k_router_logits<float>, g1, dim3(RWV * kWave), 0, st,
                        static_cast<const float*>(x), w_router, logits, counts, T, d.H, d.E);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -2,76 +2,20 @@
 // plus the shared expert as the last group):
 //   GEMM1 + SwiGLU:  h = silu(x W13[g][0:I]^T) * (x W13[g][I:2I]^T)
 //   GEMM2:           Y = h W2[g]^T
-// Each expert's weights stream from HBM once per (row tile); the tile schedule is
-// built on the device from the permute offsets, so no host synchronisation happens.
-//
-// Schedule: group g has mt_g = ceil(m_g / BM) row tiles; mt_start is their prefix
-// sum.  A GEMM with nt column tiles has mt_start[NG]*nt tiles, ordered (group,
-// column tile, row tile) so the row tiles that share one weight tile run side by
-// side.  The grid is persistent (a fixed number of workgroups per CU) and XCD-aware:
-// workgroup w runs on XCD w%8 (dispatch is round-robin over the 8 XCDs), and each
-// XCD takes one contiguous eighth of the tile list, so the workgroups of one XCD work
-// on neighbouring tiles of the same expert and share its rows through their L2.
+// Each expert's weights stream from HBM once per row tile; the tile schedule (built on
+// the device from the permute offsets, split over the XCDs by cost) is in schedule.h.
 #include "common.h"
+#include "schedule.h"
 
 namespace moe {
 namespace {
 
-constexpr int kMaxGroups = 513;
-constexpr int kSchedPer = 9;  // groups per lane of wave 0 (64 * 9 >= kMaxGroups)
-
-// Row-tile prefix sums of the groups into LDS: s_mt[g] = sum_{g' < g} ceil(m_g'/BM),
-// s_mt[NG] = total.  Wave 0 scans; the whole workgroup waits.
-__device__ __forceinline__ void build_schedule(const int32_t* __restrict__ offsets, int NG, int BM,
-                                               int* s_mt) {
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    int loc[kSchedPer];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < kSchedPer; ++i) {
-      const int g = lane * kSchedPer + i;
-      loc[i] = (g < NG) ? (offsets[g + 1] - offsets[g] + BM - 1) / BM : 0;
-      sum += loc[i];
-    }
-    int incl = sum;
-#pragma unroll
-    for (int dd = 1; dd < kWave; dd <<= 1) {
-      const int o = __shfl_up(incl, dd);
-      if (lane >= dd) incl += o;
-    }
-    int run = incl - sum;
-#pragma unroll
-    for (int i = 0; i < kSchedPer; ++i) {
-      const int g = lane * kSchedPer + i;
-      if (g < NG) s_mt[g] = run;
-      run += loc[i];
-    }
-    if (lane == kWave - 1) s_mt[NG] = incl;
-  }
-  __syncthreads();
-}
-
-// Tile decode: group by binary search over mt_start * nt.
-struct Tile {
-  int g, m_idx, n_idx;
-};
-__device__ __forceinline__ Tile decode_tile(int tile, const int32_t* mt_start, int NG, int nt) {
-  int lo = 0, hi = NG;  // find g with mt_start[g]*nt <= tile < mt_start[g+1]*nt
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (mt_start[mid] * nt <= tile) lo = mid;
-    else hi = mid;
-  }
-  const int g = lo;
-  const int mt = mt_start[g + 1] - mt_start[g];
-  const int local = tile - mt_start[g] * nt;
-  Tile r;
-  r.g = g;
-  r.n_idx = local / mt;
-  r.m_idx = local % mt;
-  return r;
-}
+using sched::build_costs;
+using sched::build_schedule;
+using sched::decode_tile;
+using sched::kMaxGroups;
+using sched::Tile;
+using sched::xcd_boundary;
 
 // XCD-aware persistent iteration: calls body(tile) for this workgroup's tiles.
 template <typename F>
@@ -209,9 +153,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
                                                       int half) {
   __shared__ __attribute__((aligned(1024))) char smem[kRing];
   __shared__ int mt_start[kMaxGroups + 1];
+  __shared__ long long s_cost[kMaxGroups + 1];
   build_schedule(offsets, NG, BM, mt_start);
   const int nt = kSwiglu ? half / 128 : (Nout + BN - 1) / BN;
-  const int ntiles = mt_start[NG] * nt;
+  build_costs(offsets, mt_start, NG, BM, nt, s_cost);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 1, wn = wv & 1;
@@ -226,9 +171,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
 
   const int P = gridDim.x, per_xcd = P / kXcds;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  const int chunk = (ntiles + kXcds - 1) / kXcds;
-  const int end = min(ntiles, (xcd + 1) * chunk);
-  for (int tile = xcd * chunk + slot; tile < end; tile += per_xcd) {
+  const int begin = xcd_boundary(xcd, offsets, mt_start, s_cost, NG, BM, nt);
+  const int end = xcd_boundary(xcd + 1, offsets, mt_start, s_cost, NG, BM, nt);
+  for (int tile = begin + slot; tile < end; tile += per_xcd) {
     Tile tl = decode_tile(tile, mt_start, NG, nt);
     tl.g = __builtin_amdgcn_readfirstlane(tl.g);
     tl.n_idx = __builtin_amdgcn_readfirstlane(tl.n_idx);

@@ -29,45 +29,21 @@
 // column l%32 and the same k of B; result element i of lane l is row
 // 8*(i/4) + 4*(l/32) + i%4, column l%32.
 #include "common.h"
+#include "schedule.h"
 
 namespace moe {
 namespace {
 
-constexpr int kMaxGroups = 513;
-constexpr int kSchedPer = 9;
+using sched::build_costs;
+using sched::build_schedule;
+using sched::decode_tile;
+using sched::kMaxGroups;
+using sched::Tile;
+using sched::xcd_boundary;
+
 constexpr int FBM = 256, FBN = 256, FBK = 128;   // FBK bytes = one 128-B line per row
 constexpr int kFB = FBN * FBK;                    // B stage: 32 KiB
 constexpr int kFRing = 3 * (128 * FBK + kFB);     // 144 KiB
-
-__device__ __forceinline__ void fp8_schedule(const int32_t* __restrict__ offsets, int NG, int BM,
-                                             int* s_mt) {
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    int loc[kSchedPer];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < kSchedPer; ++i) {
-      const int g = lane * kSchedPer + i;
-      loc[i] = (g < NG) ? (offsets[g + 1] - offsets[g] + BM - 1) / BM : 0;
-      sum += loc[i];
-    }
-    int incl = sum;
-#pragma unroll
-    for (int dd = 1; dd < kWave; dd <<= 1) {
-      const int o = __shfl_up(incl, dd);
-      if (lane >= dd) incl += o;
-    }
-    int run = incl - sum;
-#pragma unroll
-    for (int i = 0; i < kSchedPer; ++i) {
-      const int g = lane * kSchedPer + i;
-      if (g < NG) s_mt[g] = run;
-      run += loc[i];
-    }
-    if (lane == kWave - 1) s_mt[NG] = incl;
-  }
-  __syncthreads();
-}
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
@@ -94,12 +70,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(
   __shared__ __attribute__((aligned(1024))) char smem[kFRing];
   __shared__ __attribute__((aligned(16))) float s_sa[3][FBM];
   __shared__ int mt_start[kMaxGroups + 1];
-  fp8_schedule(offsets, NG, FBM, mt_start);
+  __shared__ long long s_cost[kMaxGroups + 1];
+  build_schedule(offsets, NG, FBM, mt_start);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nt = kSwiglu ? half / 128 : (Nout + FBN - 1) / FBN;
-  const int ntiles = mt_start[NG] * nt;
+  build_costs(offsets, mt_start, NG, FBM, nt, s_cost);
   const int nk = Kd / FBK;     // k steps = scale blocks along k
   const int nbr = Nrows / 128;  // weight-scale block rows
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
@@ -112,21 +89,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(
 
   const int P = gridDim.x, per_xcd = P / kXcds;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  const int chunk = (ntiles + kXcds - 1) / kXcds;
-  const int end = min(ntiles, (xcd + 1) * chunk);
-  for (int tile = xcd * chunk + slot; tile < end; tile += per_xcd) {
-    // decode (group, column tile); one row tile per 256 rows of a group
-    int lo = 0, hi = NG;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (mt_start[mid] * nt <= tile) lo = mid;
-      else hi = mid;
-    }
-    const int g = __builtin_amdgcn_readfirstlane(lo);
-    const int mt = mt_start[g + 1] - mt_start[g];
-    const int local = tile - mt_start[g] * nt;
-    const int n_idx = __builtin_amdgcn_readfirstlane(local / mt);
-    const int m_idx = __builtin_amdgcn_readfirstlane(local % mt);
+  const int begin = xcd_boundary(xcd, offsets, mt_start, s_cost, NG, FBM, nt);
+  const int end = xcd_boundary(xcd + 1, offsets, mt_start, s_cost, NG, FBM, nt);
+  for (int tile = begin + slot; tile < end; tile += per_xcd) {
+    const Tile tl = decode_tile(tile, mt_start, NG, nt);
+    const int g = __builtin_amdgcn_readfirstlane(tl.g);
+    const int n_idx = __builtin_amdgcn_readfirstlane(tl.n_idx);
+    const int m_idx = __builtin_amdgcn_readfirstlane(tl.m_idx);
     const int row0 = offsets[g];
     const int m_g = offsets[g + 1] - row0;
     const int m0 = m_idx * FBM;

@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--workload", default="v3-bf16")
     ap.add_argument("--tokens", type=int, default=0, help="override T of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--materialize", action="store_true",
+                    help="permute writes x_sorted and the gate/up GEMM reads it (default: the "
+                         "GEMM gathers its rows from x)")
     ap.add_argument("--cpu-ffn-rows", type=int, default=2048,
                     help="expert-FFN rows the oracle computes for its sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -117,7 +120,8 @@ def main():
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
     shape = Shape(T=w.T, H=w.H, E=w.E, G=w.G, M=w.M, K=w.K, J=w.J, I=w.I, S=w.S, act=w.act,
                   expert=w.expert)
-    layer = MoELayer(shape, w_router, bias, w13, w2, s13, s2, device=dev)
+    layer = MoELayer(shape, w_router, bias, w13, w2, s13, s2, device=dev,
+                     gather=not args.materialize)
     stream = torch.cuda.current_stream()
 
     names = ["route", "permute", "ffn_up", "ffn_down", "combine", "bias_update"]
@@ -185,7 +189,12 @@ def main():
     down_flops = 2.0 * R * w.I * w.H
     route_flops = 2.0 * w.T * w.E * w.H
     route_bytes = w.T * w.H * act_es + w.E * w.H * 4 + w.T * w.E * 4 * 2 + w.T * w.K * 8
-    perm_bytes = w.T * w.H * act_es + R * w.H * es + w.T * w.K * 4 * 3 + R * 4
+    if args.materialize:
+        perm_bytes = w.T * w.H * act_es + R * w.H * es + w.T * w.K * 4 * 3 + R * 4
+    else:  # index maps (+ FP8: one quantisation of x per token)
+        perm_bytes = w.T * w.K * 4 * 3 + R * 4
+        if w.expert == "e4m3":
+            perm_bytes += w.T * w.H * (act_es + 1) + w.T * (w.H // 128) * 4
     comb_bytes = R * w.H * act_es + w.T * w.H * act_es + w.T * w.K * 8
 
     def gbs(b, ms):
@@ -243,6 +252,7 @@ def main():
         "dtype": w.expert, "data": "synthetic (seeded; weights N(0,0.006), x N(0,1))",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "G": w.G, "M": w.M,
                    "K": w.K, "J": w.J, "I": w.I, "S": w.S, "act": w.act, "expert": w.expert,
+                   "dispatch": "materialized x_sorted" if args.materialize else "gather from x",
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -18,6 +18,9 @@
  *
  * One forward step is five calls on one stream:
  *   moe_route -> moe_permute -> moe_expert_ffn -> moe_combine, then moe_bias_update.
+ * The same step without the permuted copy of x: moe_permute with x_sorted = NULL
+ * (index maps only), [FP8: moe_quantize_act_fp8], moe_expert_ffn_up_gather,
+ * moe_expert_ffn_down, moe_combine, moe_bias_update -- identical results.
  *
  * Conventions for every call
  *   - All tensor pointers are DEVICE pointers, row-major, contiguous, 16-byte aligned.
@@ -116,6 +119,8 @@ moe_status moe_route(const moe_problem* p, const void* x, const float* w_router,
  *                             scale = amax/448, code = RNE-saturating E4M3 of x/scale)
  *   x_sorted_scale [R,H/128] fp32 out (FP8 only, else NULL)
  *   ws           >= moe_workspace_bytes(p, MOE_CALL_PERMUTE) bytes
+ * x_sorted = NULL: only offsets, sorted_token and inv_perm are written (x and
+ * x_sorted_scale are then not used), for moe_expert_ffn_up_gather.
  * Deterministic: every output is a pure function of the inputs. */
 moe_status moe_permute(const moe_problem* p, const void* x, const int32_t* topk_idx,
                        int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm,
@@ -155,6 +160,28 @@ moe_status moe_expert_ffn_up(const moe_problem* p, const void* x_sorted,
                              const float* x_sorted_scale, const int32_t* offsets,
                              const void* w13, const float* w13_scale, void* h, float* h_scale,
                              void* stream);
+
+/* moe_expert_ffn_up reading its rows from the unpermuted input: row r of the permuted
+ * order is row sorted_token[r] of x (the row copy of the dispatch step, fused into the
+ * GEMM's loads).  h and h_scale are identical to moe_expert_ffn_up on the x_sorted that
+ * moe_permute would have written.
+ *   x        [T,H] act_dtype, or E4M3 codes from moe_quantize_act_fp8 (FP8)
+ *   x_scale  [T,H/128] fp32 from moe_quantize_act_fp8 (FP8 only, else NULL)
+ *   sorted_token, offsets  from moe_permute
+ * Extra limit (checked): T*H*(bytes per x element) < 2^31 - 16. */
+moe_status moe_expert_ffn_up_gather(const moe_problem* p, const void* x, const float* x_scale,
+                                    const int32_t* sorted_token, const int32_t* offsets,
+                                    const void* w13, const float* w13_scale, void* h,
+                                    float* h_scale, void* stream);
+
+/* Per-token FP8 quantisation of x for moe_expert_ffn_up_gather (the quantisation
+ * moe_permute applies to each row of x_sorted, done once per token; mpbf.cn section
+ * 3.1, activations scaled per 1x128 tile): scale = amax/448 per (token, 128 columns),
+ * 1 for an all-zero tile; code = RNE-saturating E4M3 of x/scale.
+ *   x [T,H] bf16; x_q [T,H] E4M3 codes out; x_scale [T,H/128] fp32 out.
+ * Requires act_dtype BF16 and expert_dtype FP8_E4M3. */
+moe_status moe_quantize_act_fp8(const moe_problem* p, const void* x, void* x_q, float* x_scale,
+                                void* stream);
 
 /* Second half of moe_expert_ffn: Y = h W2[g]^T per group, rounded to act_dtype.
  *   h, h_scale from moe_expert_ffn_up; w2, w2_scale, offsets as moe_expert_ffn;

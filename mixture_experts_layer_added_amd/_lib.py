@@ -18,8 +18,9 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_EXPERT_FFN = 0, 1, 2
 
 EXPORTS = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_up",
-           "moe_expert_ffn_down", "moe_combine", "moe_bias_update", "moe_quantize_weights_fp8",
-           "moe_workspace_bytes", "moe_status_str", "moe_last_error")
+           "moe_expert_ffn_up_gather", "moe_quantize_act_fp8", "moe_expert_ffn_down",
+           "moe_combine", "moe_bias_update", "moe_quantize_weights_fp8", "moe_workspace_bytes",
+           "moe_status_str", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -45,6 +46,10 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m mixture_experts_layer_added_amd.build`")
+        # libmoe and torch must share one HIP runtime.  torch ships its own copy under
+        # the same soname (libamdhip64.so.7); the first copy loaded serves the whole
+        # process, so torch's is loaded before libmoe resolves its dependency.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         vp, sz, i32, i64, f32 = (ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64,
                                  ctypes.c_float)
@@ -53,6 +58,8 @@ def lib():
         L.moe_permute.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_expert_ffn.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_expert_ffn_up.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_expert_ffn_up_gather.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_quantize_act_fp8.argtypes = [pp, vp, vp, vp, vp]
         L.moe_expert_ffn_down.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_combine.argtypes = [pp, vp, vp, vp, vp, vp]
         L.moe_bias_update.argtypes = [pp, vp, f32, vp, vp]
@@ -64,8 +71,8 @@ def lib():
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         for n in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_up",
-                  "moe_expert_ffn_down", "moe_combine", "moe_bias_update",
-                  "moe_quantize_weights_fp8"):
+                  "moe_expert_ffn_up_gather", "moe_quantize_act_fp8", "moe_expert_ffn_down",
+                  "moe_combine", "moe_bias_update", "moe_quantize_weights_fp8"):
             getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -133,6 +140,19 @@ def moe_expert_ffn_up(p, x_sorted, x_sorted_scale, offsets, w13, w13_scale, h, h
     _check(lib().moe_expert_ffn_up(ctypes.byref(p), _ptr(x_sorted), _ptr(x_sorted_scale),
                                    _ptr(offsets), _ptr(w13), _ptr(w13_scale), _ptr(h),
                                    _ptr(h_scale), _stream(stream)), "moe_expert_ffn_up")
+
+
+def moe_expert_ffn_up_gather(p, x, x_scale, sorted_token, offsets, w13, w13_scale, h,
+                             h_scale=None, stream=None):
+    _check(lib().moe_expert_ffn_up_gather(ctypes.byref(p), _ptr(x), _ptr(x_scale),
+                                          _ptr(sorted_token), _ptr(offsets), _ptr(w13),
+                                          _ptr(w13_scale), _ptr(h), _ptr(h_scale),
+                                          _stream(stream)), "moe_expert_ffn_up_gather")
+
+
+def moe_quantize_act_fp8(p, x, x_q, x_scale, stream=None):
+    _check(lib().moe_quantize_act_fp8(ctypes.byref(p), _ptr(x), _ptr(x_q), _ptr(x_scale),
+                                      _stream(stream)), "moe_quantize_act_fp8")
 
 
 def moe_expert_ffn_down(p, h, h_scale, offsets, w2, w2_scale, y_sorted, stream=None):

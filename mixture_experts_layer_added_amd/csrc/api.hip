@@ -162,12 +162,14 @@ moe_status moe_permute(const moe_problem* p, const void* x, const int32_t* topk_
   Dims d;
   moe_status s = validate(p, &d);
   if (s != MOE_OK) return s;
-  REQUIRE_PTR(x);
-  REQUIRE_PTR(x_sorted);
   if (!topk_idx || !offsets || !sorted_token || !inv_perm)
     return fail(MOE_ERR_INVALID_ARG, "topk_idx, offsets, sorted_token and inv_perm are required");
-  if (d.expert == MOE_FP8_E4M3 && !x_sorted_scale)
-    return fail(MOE_ERR_INVALID_ARG, "x_sorted_scale is required for the FP8 path");
+  if (x_sorted) {  // NULL: index maps only
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(x_sorted);
+    if (d.expert == MOE_FP8_E4M3 && !x_sorted_scale)
+      return fail(MOE_ERR_INVALID_ARG, "x_sorted_scale is required for the FP8 path");
+  }
   if (!ws || ws_bytes < permute_ws_bytes(d))
     return fail(MOE_ERR_WORKSPACE, "permute needs %zu workspace bytes, got %zu",
                 permute_ws_bytes(d), ws ? ws_bytes : (size_t)0);
@@ -191,11 +193,52 @@ moe_status moe_expert_ffn_up(const moe_problem* p, const void* x_sorted,
   if (d.expert == MOE_FP8_E4M3 && (!x_sorted_scale || !w13_scale || !h_scale))
     return fail(MOE_ERR_INVALID_ARG, "the FP8 path needs x_sorted_scale, w13_scale, h_scale");
   if ((s = check_device(nullptr)) != MOE_OK) return s;
-  hipError_t e = launch_ffn_up(d, x_sorted, x_sorted_scale, offsets, w13, w13_scale, h, h_scale,
-                               static_cast<hipStream_t>(stream));
+  hipError_t e = launch_ffn_up(d, x_sorted, x_sorted_scale, offsets, nullptr, w13, w13_scale, h,
+                               h_scale, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported)
     return fail(MOE_ERR_UNSUPPORTED, "no expert FFN kernel for expert dtype %d", d.expert);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn_up launch");
+}
+
+moe_status moe_expert_ffn_up_gather(const moe_problem* p, const void* x, const float* x_scale,
+                                    const int32_t* sorted_token, const int32_t* offsets,
+                                    const void* w13, const float* w13_scale, void* h,
+                                    float* h_scale, void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w13);
+  REQUIRE_PTR(h);
+  if (!offsets || !sorted_token)
+    return fail(MOE_ERR_INVALID_ARG, "offsets and sorted_token are required");
+  if (d.expert == MOE_FP8_E4M3 && (!x_scale || !w13_scale || !h_scale))
+    return fail(MOE_ERR_INVALID_ARG, "the FP8 path needs x_scale, w13_scale, h_scale");
+  const int es = d.expert == MOE_FP8_E4M3 ? 1 : (d.expert == MOE_F32 ? 4 : 2);
+  if (d.T * (int64_t)d.H * es >= ((int64_t)1 << 31) - 16)
+    return fail(MOE_ERR_INVALID_ARG, "T*H*%d must be < 2^31 - 16 (32-bit row offsets)", es);
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  hipError_t e = launch_ffn_up(d, x, x_scale, offsets, sorted_token, w13, w13_scale, h, h_scale,
+                               static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported)
+    return fail(MOE_ERR_UNSUPPORTED, "no expert FFN kernel for expert dtype %d", d.expert);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn_up_gather launch");
+}
+
+moe_status moe_quantize_act_fp8(const moe_problem* p, const void* x, void* x_q, float* x_scale,
+                                void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  if (d.expert != MOE_FP8_E4M3 || d.act != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "moe_quantize_act_fp8 needs act BF16 and expert FP8_E4M3");
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(x_q);
+  if (!x_scale) return fail(MOE_ERR_INVALID_ARG, "x_scale is NULL");
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  hipError_t e = launch_quantize_act(d, static_cast<const uint16_t*>(x), static_cast<uint8_t*>(x_q),
+                                     x_scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_act_fp8 launch");
 }
 
 moe_status moe_expert_ffn_down(const moe_problem* p, const void* h, const float* h_scale,

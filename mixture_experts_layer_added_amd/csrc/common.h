@@ -105,21 +105,26 @@ hipError_t launch_route(const Dims& d, const void* x, const float* w_router, con
                         hipStream_t st);
 
 size_t permute_ws_bytes(const Dims& d);
+// x_sorted == nullptr: only offsets, sorted_token and inv_perm are written
 hipError_t launch_permute(const Dims& d, const void* x, const int32_t* idx, int32_t* offsets,
                           int32_t* sorted_token, int32_t* inv_perm, void* x_sorted,
                           float* x_scale, void* ws, hipStream_t st);
 
 size_t ffn_ws_bytes(const Dims& d);
 float* ffn_ws_h_scale(const Dims& d, void* ws);
+// gather: nullptr (xs is the permuted x_sorted) or sorted_token (xs is the unpermuted
+// input, [T, H], and row r of the permuted order is xs row gather[r])
 hipError_t launch_ffn_up(const Dims& d, const void* xs, const float* xs_scale,
-                         const int32_t* offsets, const void* w13, const float* w13_scale, void* h,
-                         float* h_scale, hipStream_t st);
+                         const int32_t* offsets, const int32_t* gather, const void* w13,
+                         const float* w13_scale, void* h, float* h_scale, hipStream_t st);
 hipError_t launch_ffn_down(const Dims& d, const void* h, const float* h_scale,
                            const int32_t* offsets, const void* w2, const float* w2_scale, void* ys,
                            hipStream_t st);
 hipError_t launch_fp8_up(const Dims& d, const void* xs, const float* xs_scale,
-                         const int32_t* offsets, const void* w13, const float* w13_scale, void* h,
-                         float* h_scale, hipStream_t st);
+                         const int32_t* offsets, const int32_t* gather, const void* w13,
+                         const float* w13_scale, void* h, float* h_scale, hipStream_t st);
+hipError_t launch_quantize_act(const Dims& d, const uint16_t* x, uint8_t* xq, float* x_scale,
+                               hipStream_t st);
 hipError_t launch_fp8_down(const Dims& d, const void* h, const float* h_scale,
                            const int32_t* offsets, const void* w2, const float* w2_scale, void* ys,
                            hipStream_t st);

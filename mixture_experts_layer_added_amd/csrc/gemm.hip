@@ -37,7 +37,8 @@ __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a));
 template <bool kSwiglu>
 __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
                                                   const float* __restrict__ B, float* __restrict__ C,
-                                                  const int32_t* __restrict__ offsets, int NG,
+                                                  const int32_t* __restrict__ offsets,
+                                                  const int32_t* __restrict__ gather, int NG,
                                                   int Kd, int Nrows, int Nout, int half) {
   constexpr int BM = 64, BN = 64, BK = 16;
   __shared__ __attribute__((aligned(16))) float As[BK][BM];
@@ -54,7 +55,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
     const int m0 = tl.m_idx * BM;
     // loader: thread -> (row tid/4, k (tid%4)*4)
     const int lr = tid >> 2, lk = (tid & 3) * 4;
-    const float* ap = A + (int64_t)(row0 + min(m0 + lr, m_g - 1)) * Kd + lk;
+    const int arow = row0 + min(m0 + lr, m_g - 1);
+    const float* ap = A + (int64_t)(gather ? gather[arow] : arow) * Kd + lk;
     int brow;
     if (kSwiglu) brow = lr < 32 ? tl.n_idx * 32 + lr : half + tl.n_idx * 32 + (lr - 32);
     else brow = tl.n_idx * BN + lr;
@@ -144,13 +146,16 @@ constexpr int kRing = 3 * (128 * kRowBytes + kBStage);  // 144 KiB
 // 16 distinct bank groups
 __device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ (r >> 1)) & 7) * 16; }
 
+// gather != nullptr: row r of the permuted order is row gather[r] of A (a_rows rows),
+// so the activation rows are read from the unpermuted input.
 template <bool kSwiglu>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict__ A,
                                                       const uint16_t* __restrict__ B,
                                                       uint16_t* __restrict__ C,
                                                       const int32_t* __restrict__ offsets,
-                                                      int NG, int Kd, int Nrows, int Nout,
-                                                      int half) {
+                                                      const int32_t* __restrict__ gather,
+                                                      int a_rows, int NG, int Kd, int Nrows,
+                                                      int Nout, int half) {
   __shared__ __attribute__((aligned(1024))) char smem[kRing];
   __shared__ int mt_start[kMaxGroups + 1];
   __shared__ long long s_cost[kMaxGroups + 1];
@@ -192,13 +197,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
     const int per_stage = nA + 4;  // loads per thread per stage
 
     // A rows past the expert's end and B rows past Nout read as zeros (range check)
-    const i32x4 arsrc = buffer_rsrc(A + (int64_t)(row0 + m0) * Kd, (uint32_t)m_rows * Kd * 2);
+    const i32x4 arsrc =
+        gather ? buffer_rsrc(A, (uint32_t)a_rows * Kd * 2)
+               : buffer_rsrc(A + (int64_t)(row0 + m0) * Kd, (uint32_t)m_rows * Kd * 2);
     const i32x4 brsrc = buffer_rsrc(B + (int64_t)tl.g * Nrows * Kd, (uint32_t)Nrows * Kd * 2);
     uint32_t aoff[4], boff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 64 * i + 8 * wv + lrow;
-      aoff[i] = (uint32_t)(r * Kd + lchunk * 8) * 2;
+      if (gather)
+        aoff[i] = r < m_rows ? (uint32_t)(gather[row0 + m0 + r] * Kd + lchunk * 8) * 2 : 0x7ffffff0u;
+      else
+        aoff[i] = (uint32_t)(r * Kd + lchunk * 8) * 2;
       int br;
       if (kSwiglu) br = r < 128 ? tl.n_idx * 128 + r : half + tl.n_idx * 128 + (r - 128);
       else br = tl.n_idx * BN + r;
@@ -319,23 +329,24 @@ float* ffn_ws_h_scale(const Dims& d, void* ws) {
 }
 
 hipError_t launch_ffn_up(const Dims& d, const void* xs, const float* xs_scale,
-                         const int32_t* offsets, const void* w13, const float* w13_scale, void* h,
-                         float* h_scale, hipStream_t st) {
+                         const int32_t* offsets, const int32_t* gather, const void* w13,
+                         const float* w13_scale, void* h, float* h_scale, hipStream_t st) {
   const int NG = d.E + d.S;
   const int cus = device_cu_count();
   if (d.expert == MOE_F32) {
     hipLaunchKernelGGL(k_gemm_f32<true>, dim3(persistent_grid(cus, 4)), dim3(256), 0, st,
                        static_cast<const float*>(xs), static_cast<const float*>(w13),
-                       static_cast<float*>(h), offsets, NG, d.H, 2 * d.I, d.I, d.I);
+                       static_cast<float*>(h), offsets, gather, NG, d.H, 2 * d.I, d.I, d.I);
     return hipGetLastError();
   }
   if (d.expert == MOE_BF16) {
     hipLaunchKernelGGL(k_gemm_bf16<true>, dim3(persistent_grid(cus, 1)), dim3(512), 0, st,
                        static_cast<const uint16_t*>(xs), static_cast<const uint16_t*>(w13),
-                       static_cast<uint16_t*>(h), offsets, NG, d.H, 2 * d.I, d.I, d.I);
+                       static_cast<uint16_t*>(h), offsets, gather, (int)d.T, NG, d.H, 2 * d.I,
+                       d.I, d.I);
     return hipGetLastError();
   }
-  return launch_fp8_up(d, xs, xs_scale, offsets, w13, w13_scale, h, h_scale, st);
+  return launch_fp8_up(d, xs, xs_scale, offsets, gather, w13, w13_scale, h, h_scale, st);
 }
 
 hipError_t launch_ffn_down(const Dims& d, const void* h, const float* h_scale,
@@ -346,13 +357,13 @@ hipError_t launch_ffn_down(const Dims& d, const void* h, const float* h_scale,
   if (d.expert == MOE_F32) {
     hipLaunchKernelGGL(k_gemm_f32<false>, dim3(persistent_grid(cus, 4)), dim3(256), 0, st,
                        static_cast<const float*>(h), static_cast<const float*>(w2),
-                       static_cast<float*>(ys), offsets, NG, d.I, d.H, d.H, 0);
+                       static_cast<float*>(ys), offsets, nullptr, NG, d.I, d.H, d.H, 0);
     return hipGetLastError();
   }
   if (d.expert == MOE_BF16) {
     hipLaunchKernelGGL(k_gemm_bf16<false>, dim3(persistent_grid(cus, 1)), dim3(512), 0, st,
                        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w2),
-                       static_cast<uint16_t*>(ys), offsets, NG, d.I, d.H, d.H, 0);
+                       static_cast<uint16_t*>(ys), offsets, nullptr, 0, NG, d.I, d.H, d.H, 0);
     return hipGetLastError();
   }
   return launch_fp8_down(d, h, h_scale, offsets, w2, w2_scale, ys, st);

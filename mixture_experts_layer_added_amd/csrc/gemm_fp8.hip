@@ -61,12 +61,15 @@ __device__ __forceinline__ i32x8 frag32(const char* p0, const char* p1) {
   return f;
 }
 
+// gather != nullptr: row r of the permuted order is row gather[r] of A and A_scale
+// (a_rows rows), so the activation rows are read from the unpermuted input.
 template <bool kSwiglu>
 __global__ __launch_bounds__(512, 1) void k_gemm_fp8(
     const uint8_t* __restrict__ A, const float* __restrict__ A_scale,
     const uint8_t* __restrict__ B, const float* __restrict__ B_scale, void* __restrict__ C,
-    float* __restrict__ C_scale, const int32_t* __restrict__ offsets, int NG, int Kd, int Nrows,
-    int Nout, int half) {
+    float* __restrict__ C_scale, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ gather, int a_rows, int NG, int Kd, int Nrows, int Nout,
+    int half) {
   __shared__ __attribute__((aligned(1024))) char smem[kFRing];
   __shared__ __attribute__((aligned(16))) float s_sa[3][FBM];
   __shared__ int mt_start[kMaxGroups + 1];
@@ -108,20 +111,31 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(
     const bool ld_sa = wv < nA;  // waves 0..nA-1 bring 64 activation scales each
     const int per_stage = nA + 4 + (ld_sa ? 1 : 0);
 
-    const i32x4 arsrc = buffer_rsrc(A + (int64_t)(row0 + m0) * Kd, (uint32_t)m_rows * Kd);
+    const i32x4 arsrc = gather ? buffer_rsrc(A, (uint32_t)a_rows * Kd)
+                               : buffer_rsrc(A + (int64_t)(row0 + m0) * Kd, (uint32_t)m_rows * Kd);
     const i32x4 brsrc = buffer_rsrc(B + (int64_t)g * Nrows * Kd, (uint32_t)Nrows * Kd);
-    const i32x4 srsrc = buffer_rsrc(A_scale + (int64_t)(row0 + m0) * nk, (uint32_t)m_rows * nk * 4);
+    const i32x4 srsrc =
+        gather ? buffer_rsrc(A_scale, (uint32_t)a_rows * nk * 4)
+               : buffer_rsrc(A_scale + (int64_t)(row0 + m0) * nk, (uint32_t)m_rows * nk * 4);
     uint32_t aoff[4], boff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 64 * i + 8 * wv + lrow;
-      aoff[i] = (uint32_t)(r * Kd + lchunk * 16);
+      if (gather)
+        aoff[i] = r < m_rows ? (uint32_t)(gather[row0 + m0 + r] * Kd + lchunk * 16) : 0x7ffffff0u;
+      else
+        aoff[i] = (uint32_t)(r * Kd + lchunk * 16);
       int br;
       if (kSwiglu) br = r < 128 ? n_idx * 128 + r : half + n_idx * 128 + (r - 128);
       else br = n_idx * FBN + r;
       boff[i] = br < Nrows ? (uint32_t)(br * Kd + lchunk * 16) : 0x7ffffff0u;
     }
-    const uint32_t soff = (uint32_t)((64 * wv + lane) * nk) * 4;
+    const int srow = 64 * wv + lane;  // activation-scale row this lane brings
+    uint32_t soff;
+    if (gather)
+      soff = srow < m_rows ? (uint32_t)(gather[row0 + m0 + srow] * nk) * 4 : 0x7ffffff0u;
+    else
+      soff = (uint32_t)(srow * nk) * 4;
     const uint32_t ldsw = lds0 + 8 * wv * FBK;
     const uint32_t ldss = lds_sa + 64 * wv * 4;
     // weight-scale block rows: up: gate block n_idx (tiles n even), up block
@@ -262,11 +276,12 @@ int fp8_grid(int cus) {
 }  // namespace
 
 hipError_t launch_fp8_up(const Dims& d, const void* xs, const float* xs_scale,
-                         const int32_t* offsets, const void* w13, const float* w13_scale, void* h,
-                         float* h_scale, hipStream_t st) {
+                         const int32_t* offsets, const int32_t* gather, const void* w13,
+                         const float* w13_scale, void* h, float* h_scale, hipStream_t st) {
   hipLaunchKernelGGL((k_gemm_fp8<true>), dim3(fp8_grid(device_cu_count())), dim3(512), 0, st,
                      static_cast<const uint8_t*>(xs), xs_scale, static_cast<const uint8_t*>(w13),
-                     w13_scale, h, h_scale, offsets, d.E + d.S, d.H, 2 * d.I, d.I, d.I);
+                     w13_scale, h, h_scale, offsets, gather, (int)d.T, d.E + d.S, d.H, 2 * d.I,
+                     d.I, d.I);
   return hipGetLastError();
 }
 
@@ -275,7 +290,7 @@ hipError_t launch_fp8_down(const Dims& d, const void* h, const float* h_scale,
                            hipStream_t st) {
   hipLaunchKernelGGL((k_gemm_fp8<false>), dim3(fp8_grid(device_cu_count())), dim3(512), 0, st,
                      static_cast<const uint8_t*>(h), h_scale, static_cast<const uint8_t*>(w2),
-                     w2_scale, ys, nullptr, offsets, d.E + d.S, d.I, d.H, d.H, 0);
+                     w2_scale, ys, nullptr, offsets, nullptr, 0, d.E + d.S, d.I, d.H, d.H, 0);
   return hipGetLastError();
 }
 

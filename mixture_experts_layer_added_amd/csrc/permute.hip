@@ -10,7 +10,10 @@
 //                      exclusive scan that gives the group offsets;
 //   3. k_perm_scatter: one workgroup per token writes its rows, the index maps and
 //                      the K+S copies of the token (FP8: quantised once per
-//                      128-column tile, scale = amax/448, RNE-saturating E4M3).
+//                      128-column tile, scale = amax/448, RNE-saturating E4M3);
+//      k_perm_index:   the index maps alone, when the expert GEMM gathers its rows
+//                      from x itself (then FP8 quantises each token once, in
+//                      k_quant_act).
 #include "common.h"
 
 namespace moe {
@@ -158,7 +161,70 @@ __global__ __launch_bounds__(256) void k_perm_scatter(
   }
 }
 
+// Index maps only: one thread per (token, k) pair and per shared row.
+__global__ __launch_bounds__(256) void k_perm_index(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ lrank,
+    const int32_t* __restrict__ boff, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_token, int32_t* __restrict__ inv_perm, int T, int E, int K,
+    int S) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nroute = (int64_t)T * K;
+  if (q < nroute) {
+    const int t = (int)(q / K);
+    const int e = idx[q];
+    int row = -1;
+    if (e >= 0 && e < E) {
+      row = offsets[e] + boff[(int64_t)(t / kBlockTok) * E + e] + lrank[q];
+      sorted_token[row] = t;
+    }
+    inv_perm[q] = row;
+  } else if (S && q < nroute + T) {
+    const int t = (int)(q - nroute);
+    sorted_token[offsets[E] + t] = t;
+  }
+}
+
+// Per-token activation quantisation (the FP8 path's x, once per token): 16 lanes per
+// 128-column tile, scale = amax/448 (1 if the tile is all zeros), RNE-saturating E4M3.
+__global__ __launch_bounds__(256) void k_quant_act(const uint16_t* __restrict__ x,
+                                                   uint8_t* __restrict__ xq,
+                                                   float* __restrict__ x_scale, int64_t nchunk) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;  // chunk of 8 values
+  const bool in = c < nchunk;  // nchunk is a multiple of 16: whole tiles per 16 lanes
+  float v[8];
+  float amax = 0.0f;
+  if (in) {
+    const uint4 u = reinterpret_cast<const uint4*>(x)[c];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
+  if (in) {
+    const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+    uint2 q;
+    q.x = pack4_e4m3(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
+    q.y = pack4_e4m3(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
+    reinterpret_cast<uint2*>(xq)[c] = q;
+    if ((c & 15) == 0) x_scale[c >> 4] = sc;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_act(const Dims& d, const uint16_t* x, uint8_t* xq, float* x_scale,
+                               hipStream_t st) {
+  const int64_t nchunk = d.T * (int64_t)d.H / 8;
+  hipLaunchKernelGGL(k_quant_act, dim3((unsigned)((nchunk + 255) / 256)), dim3(256), 0, st, x, xq,
+                     x_scale, nchunk);
+  return hipGetLastError();
+}
 
 size_t permute_ws_bytes(const Dims& d) {
   const int64_t nb = (d.T + kBlockTok - 1) / kBlockTok;
@@ -180,7 +246,11 @@ hipError_t launch_permute(const Dims& d, const void* x, const int32_t* idx, int3
                      T);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (d.expert == MOE_FP8_E4M3)
+  if (!x_sorted) {
+    const int64_t n = (int64_t)T * d.K + (d.S ? T : 0);
+    hipLaunchKernelGGL(k_perm_index, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, idx,
+                       lrank, boff, offsets, sorted_token, inv_perm, T, d.E, d.K, d.S);
+  } else if (d.expert == MOE_FP8_E4M3)
     hipLaunchKernelGGL((k_perm_scatter<true, uint16_t>), dim3(T), dim3(256), 0, st,
                        static_cast<const uint16_t*>(x), idx, lrank, boff, offsets, sorted_token,
                        inv_perm, x_sorted, x_scale, T, d.H, d.E, d.K, d.S);

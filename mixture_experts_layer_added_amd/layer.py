@@ -53,11 +53,18 @@ class MoELayer:
     Weights: w_router [E,H] fp32, bias [E] fp32 (updated in place by bias_step),
     w13 [E+S,2I,H] and w2 [E+S,H,I] in the expert dtype (uint8 E4M3 codes with
     w13_scale / w2_scale for the FP8 path).
+
+    gather=False: permute writes x_sorted and the gate/up GEMM reads it.
+    gather=True:  permute writes the index maps only (FP8: plus one quantisation of x
+    per token) and the gate/up GEMM reads its rows from x through sorted_token; the
+    results are identical and the permuted copy of x is never written.
     """
 
     def __init__(self, shape: Shape, w_router, bias, w13, w2, w13_scale=None, w2_scale=None,
-                 device="cuda"):
+                 device="cuda", gather=False):
         self.shape = shape
+        self.gather = gather
+        self._x = None
         self.p = shape.problem()
         self.w_router, self.bias = w_router, bias
         self.w13, self.w2, self.w13_scale, self.w2_scale = w13, w2, w13_scale, w2_scale
@@ -72,12 +79,16 @@ class MoELayer:
         self.offsets = torch.empty((E + shape.S + 1,), **i32)
         self.sorted_token = torch.empty((R,), **i32)
         self.inv_perm = torch.empty((T, K), **i32)
+        rows = T if gather else R  # gather: x itself (FP8: its per-token codes)
+        self.x_sorted = None
         if shape.expert == "e4m3":
-            self.x_sorted = torch.empty((R, H), dtype=torch.uint8, device=dev)
-            self.x_scale = torch.empty((R, H // 128), dtype=torch.float32, device=dev)
+            self.x_q = torch.empty((rows, H), dtype=torch.uint8, device=dev)
+            self.x_scale = torch.empty((rows, H // 128), dtype=torch.float32, device=dev)
         else:
-            self.x_sorted = torch.empty((R, H), dtype=act, device=dev)
+            self.x_q = None if gather else torch.empty((R, H), dtype=act, device=dev)
             self.x_scale = None
+        if not gather:
+            self.x_sorted = self.x_q
         if shape.expert == "e4m3":
             self.h = torch.empty((R, shape.I), dtype=torch.uint8, device=dev)
             self.h_scale = torch.empty((R, shape.I // 128), dtype=torch.float32, device=dev)
@@ -103,12 +114,25 @@ class MoELayer:
 
     def permute(self, x, stream=None):
         ws, n = self._ws(L.MOE_CALL_PERMUTE)
-        L.moe_permute(self.p, x, self.topk_idx, self.offsets, self.sorted_token, self.inv_perm,
-                      self.x_sorted, self.x_scale, ws, n, stream)
+        if self.gather:
+            L.moe_permute(self.p, x, self.topk_idx, self.offsets, self.sorted_token,
+                          self.inv_perm, None, None, ws, n, stream)
+            if self.shape.expert == "e4m3":
+                L.moe_quantize_act_fp8(self.p, x, self.x_q, self.x_scale, stream)
+            self._x = x
+        else:
+            L.moe_permute(self.p, x, self.topk_idx, self.offsets, self.sorted_token,
+                          self.inv_perm, self.x_sorted, self.x_scale, ws, n, stream)
 
     def expert_ffn_up(self, stream=None):
-        L.moe_expert_ffn_up(self.p, self.x_sorted, self.x_scale, self.offsets, self.w13,
-                            self.w13_scale, self.h, self.h_scale, stream)
+        if self.gather:
+            xin = self.x_q if self.shape.expert == "e4m3" else self._x
+            L.moe_expert_ffn_up_gather(self.p, xin, self.x_scale, self.sorted_token,
+                                       self.offsets, self.w13, self.w13_scale, self.h,
+                                       self.h_scale, stream)
+        else:
+            L.moe_expert_ffn_up(self.p, self.x_sorted, self.x_scale, self.offsets, self.w13,
+                                self.w13_scale, self.h, self.h_scale, stream)
 
     def expert_ffn_down(self, stream=None):
         L.moe_expert_ffn_down(self.p, self.h, self.h_scale, self.offsets, self.w2, self.w2_scale,

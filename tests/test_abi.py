@@ -133,3 +133,27 @@ def test_binding_has_no_fallback(L, monkeypatch):
     monkeypatch.setattr(L, "LIB_PATH", "/nonexistent/libmoe.so")
     with pytest.raises(RuntimeError):
         L.lib()
+
+
+def test_gather_entry_points_validate(L):
+    lib = L.lib()
+    d = ctypes.c_void_p(4096)
+    p = prob(L, act_dtype=1, expert_dtype=1)
+    rc = lib.moe_expert_ffn_up_gather(ctypes.byref(p), d, None, None, d, d, None, d, None, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "sorted_token" in L.last_error()
+    rc = lib.moe_expert_ffn_up_gather(ctypes.byref(p), None, None, d, d, d, None, d, None, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "x is NULL" in L.last_error()
+    big = prob(L, T=200000, H=7168, I=128, act_dtype=1, expert_dtype=1)
+    rc = lib.moe_expert_ffn_up_gather(ctypes.byref(big), d, None, d, d, d, None, d, None, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "2^31" in L.last_error()
+    p8 = prob(L, act_dtype=1, expert_dtype=2)
+    rc = lib.moe_expert_ffn_up_gather(ctypes.byref(p8), d, None, d, d, d, None, d, None, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "x_scale" in L.last_error()
+    # activation quantisation is FP8-only
+    rc = lib.moe_quantize_act_fp8(ctypes.byref(p), d, d, d, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "FP8" in L.last_error()
+    rc = lib.moe_quantize_act_fp8(ctypes.byref(p8), d, d, None, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "x_scale" in L.last_error()
+    # permute without x_sorted needs no x
+    rc = lib.moe_permute(ctypes.byref(p), None, None, d, d, d, None, None, d, 1 << 20, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "topk_idx" in L.last_error()

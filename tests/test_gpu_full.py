@@ -35,7 +35,7 @@ def np_(t):
     return workloads.to_numpy(t)
 
 
-def build(w, fp8=False):
+def build(w, fp8=False, gather=False):
     from mixture_experts_layer_added_amd.layer import MoELayer, quantize_weights_fp8
     dev = torch.device("cuda")
     wr, b = workloads.make_router(w, dev)
@@ -44,8 +44,8 @@ def build(w, fp8=False):
     if fp8:
         q13, s13 = quantize_weights_fp8(w13)
         q2, s2 = quantize_weights_fp8(w2)
-        return MoELayer(shape_of(w), wr, b, q13, q2, s13, s2), (w13, w2)
-    return MoELayer(shape_of(w), wr, b, w13, w2), (w13, w2)
+        return MoELayer(shape_of(w), wr, b, q13, q2, s13, s2, gather=gather), (w13, w2)
+    return MoELayer(shape_of(w), wr, b, w13, w2, gather=gather), (w13, w2)
 
 
 def check_routing(w, layer, x):
@@ -65,12 +65,22 @@ def check_routing(w, layer, x):
     assert np.array_equal(np_(layer.sorted_token), st)
     assert np.array_equal(np_(layer.inv_perm), inv)
     rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([rng.integers(0, w.R, 3000), [0, w.R - 1, w.T * w.K]]))
-    got = np_(layer.x_sorted[torch.from_numpy(rows).cuda()])
-    assert np.array_equal(got.view(np.uint8), xs[rows].view(np.uint8))
-    if fp8:
-        gsc = np_(layer.x_scale[torch.from_numpy(rows).cuda()])
-        assert np.array_equal(gsc.view(np.uint32), xsc[rows].view(np.uint32))
+    if layer.gather:
+        # no x_sorted; FP8 codes per token (the oracle's permuted rows of those tokens)
+        if fp8:
+            tok = np.unique(np.concatenate([rng.integers(0, w.T, 500), [0, w.T - 1]]))
+            rows = w.T * w.K + tok  # shared-expert rows hold token t at T*K + t
+            g = torch.from_numpy(tok).cuda()
+            assert np.array_equal(np_(layer.x_q[g]), xs[rows])
+            assert np.array_equal(np_(layer.x_scale[g]).view(np.uint32),
+                                  xsc[rows].view(np.uint32))
+    else:
+        rows = np.unique(np.concatenate([rng.integers(0, w.R, 3000), [0, w.R - 1, w.T * w.K]]))
+        got = np_(layer.x_sorted[torch.from_numpy(rows).cuda()])
+        assert np.array_equal(got.view(np.uint8), xs[rows].view(np.uint8))
+        if fp8:
+            gsc = np_(layer.x_scale[torch.from_numpy(rows).cuda()])
+            assert np.array_equal(gsc.view(np.uint32), xsc[rows].view(np.uint32))
     log(f"    routing/permutation bit-exact for all {w.T} tokens; "
         f"loads min/max {counts.min()}/{counts.max()} (mean {w.T * w.K / w.E:.1f})")
     return idx, gate, counts, inv, xs, xsc
@@ -137,11 +147,14 @@ def check_sampled_outputs(w, layer, idx, gate, inv, xs, xsc, wts, tokens):
     assert e1 <= TOL[w.expert] and e2 <= TOL[w.expert]
 
 
-@pytest.mark.parametrize("name,n_tok", [("v3-bf16", 10), ("v3-decode", 8), ("v3-fp8", 6)])
-def test_full_shape_forward(name, n_tok):
+@pytest.mark.parametrize("name,n_tok,gather", [("v3-bf16", 10, False), ("v3-decode", 8, False),
+                                               ("v3-fp8", 6, False), ("v3-bf16", 6, True),
+                                               ("v3-fp8", 4, True), ("v3-decode", 6, True)])
+def test_full_shape_forward(name, n_tok, gather):
     w = workloads.get(name)
-    log(f"[full] {name}: T={w.T} H={w.H} E={w.E}+{w.S} K={w.K} I={w.I} expert={w.expert}")
-    layer, wts = build(w, fp8=w.expert == "e4m3")
+    log(f"[full] {name}: T={w.T} H={w.H} E={w.E}+{w.S} K={w.K} I={w.I} expert={w.expert} "
+        f"gather={gather}")
+    layer, wts = build(w, fp8=w.expert == "e4m3", gather=gather)
     x = workloads.make_x(w, device="cuda")
     layer.forward(x)
     torch.cuda.synchronize()

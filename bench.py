@@ -47,7 +47,7 @@ def kernel_source_sha(expert):
     return h.hexdigest()
 
 
-def measured_traffic(workload, expert):
+def measured_traffic(workload, expert, dispatch):
     """HBM bytes per gate/up launch from the committed FETCH_SIZE / WRITE_SIZE counter
     summary of this workload, or None when there is none or the kernel source has changed
     since the counters were taken."""
@@ -61,6 +61,8 @@ def measured_traffic(workload, expert):
     rec = json.loads(m.group(1))
     if rec.get("source_sha256") != kernel_source_sha(expert):
         return None, "kernel changed since the counters were taken"
+    if rec.get("dispatch") != dispatch:
+        return None, f"counters were taken with dispatch '{rec.get('dispatch')}'"
     return int(rec["fetch_bytes"] + rec["write_bytes"]), path[len(ROOT) + 1:]
 
 
@@ -227,7 +229,8 @@ def main():
                 "unit": "GB/s", "frac": round(up_gbs / HBM_PEAK_GBS, 4),
                 "bytes_per_launch": up_bytes, "ms_per_launch": round(avg_ms["ffn_up"], 4),
                 "traffic": None}
-    traffic, src = measured_traffic(w.name, w.expert)
+    dispatch = "materialized x_sorted" if args.materialize else "gather from x"
+    traffic, src = measured_traffic(w.name, w.expert, dispatch)
     roofline["traffic"] = traffic
     roofline["traffic_source"] = src
     roofline["kernel_source_sha256"] = kernel_source_sha(w.expert)
@@ -252,7 +255,7 @@ def main():
         "dtype": w.expert, "data": "synthetic (seeded; weights N(0,0.006), x N(0,1))",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "G": w.G, "M": w.M,
                    "K": w.K, "J": w.J, "I": w.I, "S": w.S, "act": w.act, "expert": w.expert,
-                   "dispatch": "materialized x_sorted" if args.materialize else "gather from x",
+                   "dispatch": dispatch,
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,

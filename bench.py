@@ -303,7 +303,9 @@ def cpu_baseline(w, layer, x, w_router, bias, w13, w2, ffn_rows):
         if n > 0:
             sample.append((g, np.arange(off[g], off[g] + n)))
             taken += n
-    sample.append((w.E, np.arange(off[w.E], off[w.E] + half)))
+    if w.S:
+        n_shared = min(half, w.T)
+        sample.append((w.E, np.arange(off[w.E], off[w.E] + n_shared)))
     out_dt = oracle.BF16 if w.act == "bf16" else oracle.F32
     t_ffn_sample = 0.0
     n_rows = 0
@@ -320,7 +322,8 @@ def cpu_baseline(w, layer, x, w_router, bias, w13, w2, ffn_rows):
             oracle.expert_ffn(xs[rows], a, b, out_dt, nthreads=threads)
         t_ffn_sample += time.perf_counter() - t
         n_rows += len(rows)
-    experts = f"experts {sample[0][0]}..{sample[-2][0]} and the shared expert"
+    routed = [g for g, _ in sample if g < w.E]
+    experts = f"experts {routed[0]}..{routed[-1]}" + (" and the shared expert" if w.S else "")
     t_ffn = t_ffn_sample * (w.R / n_rows)
     ys = workloads.to_numpy(workloads.make_y_sorted(w, seed=9, device=x.device))
     t = time.perf_counter()

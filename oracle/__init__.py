@@ -75,6 +75,16 @@ def _declare(L):
     L.oracle_combine.restype = None
     L.oracle_bias_update.argtypes = [i32, i64, i32, vp, f32, vp]
     L.oracle_bias_update.restype = None
+    L.oracle_combine_backward.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32]
+    L.oracle_combine_backward.restype = None
+    L.oracle_router_backward.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, i32]
+    L.oracle_router_backward.restype = i32
+    L.oracle_expert_backward.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, i32]
+    L.oracle_expert_backward.restype = i32
+    L.oracle_unpermute_sum.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp, i32]
+    L.oracle_unpermute_sum.restype = None
     for n in ("oracle_exp_spec_array", "oracle_sigmoid_array", "oracle_e4m3_from_f32_array",
               "oracle_bf16_from_f64_array"):
         getattr(L, n).argtypes = [i64, vp, vp]
@@ -336,3 +346,108 @@ def forward(x, w_router, bias, w13, w2, G, M, K, J, shared=1, expert_dtype=None,
     return dict(topk_idx=idx, topk_gate=gate, counts=counts, offsets=offsets,
                 sorted_token=sorted_token, inv_perm=inv_perm, x_sorted=xs,
                 x_sorted_scale=xsc, y_sorted=ys, y=y)
+
+
+# --- backward (the derivative of the forward; see moe_oracle.c) ----------------
+
+def combine_backward(dy, y_sorted, inv_perm, topk_gate, shared=1, nthreads=None):
+    """Returns (dY_sorted [R,H] act dtype, dgate [T,K] f32)."""
+    dy = np.ascontiguousarray(dy)
+    y_sorted = np.ascontiguousarray(y_sorted)
+    inv_perm = _c(inv_perm, np.int32)
+    topk_gate = _c(topk_gate, np.float32)
+    T, H = dy.shape
+    K = inv_perm.shape[1]
+    dys = np.zeros_like(y_sorted)
+    dg = np.empty((T, K), np.float32)
+    lib().oracle_combine_backward(T, H, K, 1 if shared else 0, act_code(dy), _p(dy),
+                                  _p(y_sorted), _p(inv_perm), _p(topk_gate), _p(dys), _p(dg),
+                                  nthreads or default_threads())
+    return dys, dg
+
+
+def router_backward(x, w_router, logits, topk_idx, topk_gate, dgate, nthreads=None):
+    """Returns (dz [T,K] f32, dx_router [T,H] f32, dw_router [E,H] f32)."""
+    x = np.ascontiguousarray(x)
+    w_router = _c(w_router, np.float32)
+    logits = _c(logits, np.float32)
+    topk_idx = _c(topk_idx, np.int32)
+    topk_gate = _c(topk_gate, np.float32)
+    dgate = _c(dgate, np.float32)
+    T, H = x.shape
+    E = w_router.shape[0]
+    K = topk_idx.shape[1]
+    dz = np.empty((T, K), np.float32)
+    dxr = np.empty((T, H), np.float32)
+    dwr = np.empty((E, H), np.float32)
+    rc = lib().oracle_router_backward(T, H, E, K, act_code(x), _p(x), _p(w_router), _p(logits),
+                                      _p(topk_idx), _p(topk_gate), _p(dgate), _p(dz), _p(dxr),
+                                      _p(dwr), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_router_backward rejected the input")
+    return dz, dxr, dwr
+
+
+def expert_backward(x_rows, w13, w2, dy_rows, nthreads=None):
+    """One expert on a block of rows.  Returns (h, dau, dx_rows, dw13 f32, dw2 f32)."""
+    x_rows = np.ascontiguousarray(x_rows)
+    w13 = np.ascontiguousarray(w13)
+    w2 = np.ascontiguousarray(w2)
+    dy_rows = np.ascontiguousarray(dy_rows)
+    n, H = x_rows.shape
+    I = w2.shape[1]
+    dt = act_code(x_rows)
+    h = np.empty((n, I), x_rows.dtype)
+    dau = np.empty((n, 2 * I), x_rows.dtype)
+    dx = np.empty((n, H), x_rows.dtype)
+    dw13 = np.empty((2 * I, H), np.float32)
+    dw2 = np.empty((H, I), np.float32)
+    rc = lib().oracle_expert_backward(n, H, I, dt, _p(x_rows), _p(w13), _p(w2), _p(dy_rows),
+                                      _p(h), _p(dau), _p(dx), _p(dw13), _p(dw2),
+                                      nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_expert_backward rejected the input")
+    return h, dau, dx, dw13, dw2
+
+
+def unpermute_sum(dx_sorted, inv_perm, dx_router, T, shared=1, nthreads=None):
+    dx_sorted = np.ascontiguousarray(dx_sorted)
+    inv_perm = _c(inv_perm, np.int32)
+    H = dx_sorted.shape[1]
+    K = inv_perm.shape[1]
+    dxr = None if dx_router is None else _c(dx_router, np.float32)
+    dx = np.empty((T, H), dx_sorted.dtype)
+    lib().oracle_unpermute_sum(T, H, K, 1 if shared else 0, act_code(dx_sorted), _p(dx_sorted),
+                               _p(inv_perm), _p(dxr), _p(dx), nthreads or default_threads())
+    return dx
+
+
+def backward(x, w_router, w13, w2, fwd, dy, logits, shared=1, nthreads=None):
+    """Whole-layer backward from the forward's intermediates (the dict forward() returns)
+    and the output gradient dy [T,H] (act dtype).  logits [T,E] f32 are the router
+    logits of the forward.  Returns a dict: dx [T,H] act, dw_router [E,H] f32,
+    dw13 [E+S,2I,H] f32, dw2 [E+S,H,I] f32 and the intermediates."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    S = 1 if shared else 0
+    I = w2.shape[2]
+    off = fwd["offsets"]
+    dys, dg = combine_backward(dy, fwd["y_sorted"], fwd["inv_perm"], fwd["topk_gate"], shared,
+                               nthreads)
+    dz, dxr, dwr = router_backward(x, w_router, logits, fwd["topk_idx"], fwd["topk_gate"], dg,
+                                   nthreads)
+    xs = fwd["x_sorted"]
+    R = xs.shape[0]
+    dxs = np.zeros((R, H), xs.dtype)
+    dau = np.zeros((R, 2 * I), xs.dtype)
+    dw13 = np.zeros((E + S, 2 * I, H), np.float32)
+    dw2 = np.zeros((E + S, H, I), np.float32)
+    for g in range(E + S):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi == lo:
+            continue
+        _, dau[lo:hi], dxs[lo:hi], dw13[g], dw2[g] = expert_backward(xs[lo:hi], w13[g], w2[g],
+                                                                     dys[lo:hi], nthreads)
+    dx = unpermute_sum(dxs, fwd["inv_perm"], dxr, T, shared, nthreads)
+    return dict(dx=dx, dw_router=dwr, dw13=dw13, dw2=dw2, dy_sorted=dys, dgate=dg, dz=dz,
+                dx_router=dxr, dau=dau, dx_sorted=dxs)

@@ -564,3 +564,233 @@ void oracle_e4m3_from_f32_array(int64_t n, const float* v, uint8_t* out) {
 void oracle_bf16_from_f64_array(int64_t n, const double* v, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_from_f64(v[i]);
 }
+
+/* ========================================================================= */
+/* Backward of the layer (the derivative of the forward above; the pages only  */
+/* say that gradients accumulate in higher precision, that the block's input   */
+/* and weight gradients are separate computations, and -- [resmic] 核心架构三 -- */
+/* that the routing bias takes no part in back-propagation).  fp64 arithmetic; */
+/* a tensor is rounded where the layer stores it: the expert-output gradient   */
+/* dY and the SwiGLU-input gradient [da|du] at the activation dtype (they feed  */
+/* the grouped GEMMs), the permuted input gradient at the activation dtype,    */
+/* the input gradient dx at the activation dtype, weight gradients in fp32.    */
+/* ========================================================================= */
+
+static void store_act(int dtype, void* p, int64_t i, double v) {
+  if (dtype == DT_BF16) ((uint16_t*)p)[i] = oracle_bf16_from_f64(v);
+  else ((float*)p)[i] = oracle_f32_from_f64(v);
+}
+
+/* Combine backward: y[t] = Y_S[t] + sum_k g[t,k] Y[row(t,k)], so
+ *   dY[row(t,k)] = g[t,k] * dy[t],  dY[T*K + t] = dy[t]  (shared expert),
+ *   dg[t,k]      = <dy[t], Y[row(t,k)]>.                                        */
+typedef struct {
+  int64_t T; int H, K, S, dtype;
+  const void* dy; const void* ys; const int32_t* inv_perm; const float* gate;
+  void* dys; float* dgate;
+} combine_bwd_ctx;
+
+static void combine_bwd_item(void* c, int64_t t) {
+  combine_bwd_ctx* C = (combine_bwd_ctx*)c;
+  int H = C->H;
+  for (int k = 0; k < C->K; ++k) {
+    int64_t row = C->inv_perm[t * C->K + k];
+    if (row < 0) { C->dgate[t * C->K + k] = 0.0f; continue; }
+    double g = C->gate[t * C->K + k], dot = 0.0;
+    for (int m = 0; m < H; ++m) {
+      double d = load_act(C->dtype, C->dy, t * H + m);
+      dot += d * load_act(C->dtype, C->ys, row * H + m);
+      store_act(C->dtype, C->dys, row * H + m, g * d);
+    }
+    C->dgate[t * C->K + k] = oracle_f32_from_f64(dot);
+  }
+  if (C->S)
+    for (int m = 0; m < H; ++m)
+      store_act(C->dtype, C->dys, (C->T * C->K + t) * H + m,
+                load_act(C->dtype, C->dy, t * H + m));
+}
+
+void oracle_combine_backward(int64_t T, int H, int K, int S, int dtype, const void* dy,
+                             const void* y_sorted, const int32_t* inv_perm,
+                             const float* topk_gate, void* dy_sorted, float* dgate,
+                             int nthreads) {
+  combine_bwd_ctx c = {T, H, K, S, dtype, dy, y_sorted, inv_perm, topk_gate, dy_sorted, dgate};
+  parallel_for(T, nthreads, combine_bwd_item, &c);
+}
+
+/* Gate and router backward.  g_k = s_k / S with S = sum_j s_j over the chosen
+ * experts ([mpbf] 2.2: selected scores renormalised), s = sigmoid(clamp(z, +-80)):
+ *   ds_j = (dg_j - sum_k g_k dg_k) / S,   dz_j = ds_j s_j (1 - s_j)  (0 if |z| > 80),
+ *   dx_r[t] = sum_j dz_j W_r[e_j],        dW_r[e] = sum over (t,j) with e_j = e of dz_j x[t].
+ * The bias only chose the experts: it has no gradient and does not enter here.   */
+typedef struct {
+  int64_t T; int H, E, K, dtype;
+  const void* x; const float* wr; const float* z; const int32_t* idx; const float* gate;
+  const float* dgate; float* dz; float* dxr;
+} router_bwd_ctx;
+
+static void router_bwd_item(void* c, int64_t t) {
+  router_bwd_ctx* R = (router_bwd_ctx*)c;
+  int K = R->K, H = R->H;
+  double S = 0.0, gd = 0.0;
+  double s[32];
+  for (int k = 0; k < K; ++k) {
+    int e = R->idx[t * K + k];
+    s[k] = oracle_sigmoid(R->z[t * R->E + e]);
+    S += s[k];
+    gd += (double)R->gate[t * K + k] * R->dgate[t * K + k];
+  }
+  for (int k = 0; k < K; ++k) {
+    int e = R->idx[t * K + k];
+    float zz = R->z[t * R->E + e];
+    double ds = (R->dgate[t * K + k] - gd) / S;
+    double dz = (zz > 80.0f || zz < -80.0f) ? 0.0 : ds * s[k] * (1.0 - s[k]);
+    R->dz[t * K + k] = oracle_f32_from_f64(dz);
+  }
+  for (int m = 0; m < H; ++m) {
+    double acc = 0.0;
+    for (int k = 0; k < K; ++k)
+      acc += (double)R->dz[t * K + k] * R->wr[(int64_t)R->idx[t * K + k] * H + m];
+    R->dxr[t * H + m] = oracle_f32_from_f64(acc);
+  }
+}
+
+typedef struct {
+  int64_t T; int H, E, K, dtype;
+  const void* x; const int32_t* idx; const float* dz; float* dwr;
+} router_wgrad_ctx;
+
+static void router_wgrad_item(void* c, int64_t e) {
+  router_wgrad_ctx* W = (router_wgrad_ctx*)c;
+  int H = W->H;
+  double* acc = (double*)calloc(H, sizeof(double));
+  for (int64_t t = 0; t < W->T; ++t)
+    for (int k = 0; k < W->K; ++k)
+      if (W->idx[t * W->K + k] == e) {
+        double d = W->dz[t * W->K + k];
+        for (int m = 0; m < H; ++m) acc[m] += d * load_act(W->dtype, W->x, t * H + m);
+      }
+  for (int m = 0; m < H; ++m) W->dwr[e * H + m] = oracle_f32_from_f64(acc[m]);
+  free(acc);
+}
+
+/* x [T,H] act; w_router [E,H] f32; logits [T,E] f32; topk_idx/gate/dgate [T,K];
+ * out: dz [T,K] f32, dx_router [T,H] f32, dw_router [E,H] f32.  K <= 32. */
+int oracle_router_backward(int64_t T, int H, int E, int K, int dtype, const void* x,
+                           const float* w_router, const float* logits, const int32_t* topk_idx,
+                           const float* topk_gate, const float* dgate, float* dz,
+                           float* dx_router, float* dw_router, int nthreads) {
+  if (K > 32) return -1;
+  router_bwd_ctx c = {T, H, E, K, dtype, x, w_router, logits, topk_idx, topk_gate, dgate, dz,
+                      dx_router};
+  parallel_for(T, nthreads, router_bwd_item, &c);
+  router_wgrad_ctx w = {T, H, E, K, dtype, x, topk_idx, dz, dw_router};
+  parallel_for(E, nthreads, router_wgrad_item, &w);
+  return 0;
+}
+
+/* Expert FFN backward for the n rows of one group (x rows, dY rows; w13 [2I,H],
+ * w2 [H,I] of that expert):  a = x W1^T, u = x W3^T, h = silu(a) u (stored at the
+ * act dtype as in the forward),
+ *   dh  = dY W2,                  da = dh u silu'(a),  du = dh silu(a)  -> [da|du] stored,
+ *   dx  = [da|du] W13             (stored at the act dtype),
+ *   dW2 = dY^T h,  dW13 = [da|du]^T x   (fp32).
+ * silu(a) = a sigma(a), silu'(a) = sigma(a) (1 + a (1 - sigma(a))).                 */
+typedef struct {
+  int H, I, dtype;
+  const void* x; const void* w13; const void* w2; const void* dy;
+  void* hs; void* dau; void* dx;
+} ebwd_ctx;
+
+static void ebwd_row_item(void* c, int64_t r) {
+  ebwd_ctx* B = (ebwd_ctx*)c;
+  int H = B->H, I = B->I, dt = B->dtype;
+  for (int n = 0; n < I; ++n) {
+    double a = 0.0, u = 0.0, dh = 0.0;
+    for (int k = 0; k < H; ++k) {
+      double xv = dec(dt, B->x, r * H + k);
+      a += xv * dec(dt, B->w13, (int64_t)n * H + k);
+      u += xv * dec(dt, B->w13, (int64_t)(I + n) * H + k);
+    }
+    for (int m = 0; m < H; ++m)
+      dh += dec(dt, B->dy, r * H + m) * dec(dt, B->w2, (int64_t)m * I + n);
+    double sg = 1.0 / (1.0 + exp(-a));
+    store_act(dt, B->hs, r * I + n, a * sg * u);
+    store_act(dt, B->dau, r * 2 * I + n, dh * u * sg * (1.0 + a * (1.0 - sg)));
+    store_act(dt, B->dau, r * 2 * I + I + n, dh * a * sg);
+  }
+  for (int k = 0; k < H; ++k) {
+    double acc = 0.0;
+    for (int j = 0; j < 2 * I; ++j)
+      acc += dec(dt, B->dau, r * 2 * I + j) * dec(dt, B->w13, (int64_t)j * H + k);
+    store_act(dt, B->dx, r * H + k, acc);
+  }
+}
+
+typedef struct {
+  int64_t n; int H, I, dtype;
+  const void* x; const void* dy; const void* hs; const void* dau;
+  float* dw13; float* dw2;
+} ewgrad_ctx;
+
+/* item j < 2I: row j of dW13; item 2I + m: row m of dW2 */
+static void ewgrad_item(void* c, int64_t j) {
+  ewgrad_ctx* W = (ewgrad_ctx*)c;
+  int H = W->H, I = W->I, dt = W->dtype;
+  if (j < 2 * I) {
+    for (int k = 0; k < H; ++k) {
+      double acc = 0.0;
+      for (int64_t r = 0; r < W->n; ++r)
+        acc += dec(dt, W->dau, r * 2 * I + j) * dec(dt, W->x, r * H + k);
+      W->dw13[j * H + k] = oracle_f32_from_f64(acc);
+    }
+  } else {
+    int64_t m = j - 2 * I;
+    for (int n = 0; n < I; ++n) {
+      double acc = 0.0;
+      for (int64_t r = 0; r < W->n; ++r)
+        acc += dec(dt, W->dy, r * H + m) * dec(dt, W->hs, r * I + n);
+      W->dw2[m * I + n] = oracle_f32_from_f64(acc);
+    }
+  }
+}
+
+/* x [n,H], dy [n,H] act (F32 or BF16); w13 [2I,H], w2 [H,I] act;
+ * out: h [n,I] act, dau [n,2I] act, dx [n,H] act, dw13 [2I,H] f32, dw2 [H,I] f32. */
+int oracle_expert_backward(int64_t n, int H, int I, int dtype, const void* x, const void* w13,
+                           const void* w2, const void* dy, void* h, void* dau, void* dx,
+                           float* dw13, float* dw2, int nthreads) {
+  if (dtype == DT_E4M3) return -1;
+  ebwd_ctx b = {H, I, dtype, x, w13, w2, dy, h, dau, dx};
+  parallel_for(n, nthreads, ebwd_row_item, &b);
+  ewgrad_ctx w = {n, H, I, dtype, x, dy, h, dau, dw13, dw2};
+  parallel_for(2 * I + H, nthreads, ewgrad_item, &w);
+  return 0;
+}
+
+/* Input gradient: dx[t] = dx_router[t] + sum_k dx_sorted[row(t,k)] + dx_sorted[T*K+t]
+ * (the last term if a shared expert exists), summed in fp64, rounded to the act dtype. */
+typedef struct {
+  int64_t T; int H, K, S, dtype;
+  const void* dxs; const int32_t* inv_perm; const float* dxr; void* dx;
+} unperm_ctx;
+
+static void unperm_item(void* c, int64_t t) {
+  unperm_ctx* U = (unperm_ctx*)c;
+  for (int m = 0; m < U->H; ++m) {
+    double acc = U->dxr ? U->dxr[t * U->H + m] : 0.0;
+    for (int k = 0; k < U->K; ++k) {
+      int64_t row = U->inv_perm[t * U->K + k];
+      if (row >= 0) acc += load_act(U->dtype, U->dxs, row * U->H + m);
+    }
+    if (U->S) acc += load_act(U->dtype, U->dxs, (U->T * U->K + t) * U->H + m);
+    store_act(U->dtype, U->dx, t * U->H + m, acc);
+  }
+}
+
+void oracle_unpermute_sum(int64_t T, int H, int K, int S, int dtype, const void* dx_sorted,
+                          const int32_t* inv_perm, const float* dx_router, void* dx,
+                          int nthreads) {
+  unperm_ctx c = {T, H, K, S, dtype, dx_sorted, inv_perm, dx_router, dx};
+  parallel_for(T, nthreads, unperm_item, &c);
+}

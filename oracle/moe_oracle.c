@@ -576,6 +576,12 @@ void oracle_bf16_from_f64_array(int64_t n, const double* v, uint16_t* out) {
 /* the input gradient dx at the activation dtype, weight gradients in fp32.    */
 /* ========================================================================= */
 
+/* v rounded to the activation dtype (round to nearest even) and widened again */
+static double act_round(int dtype, double v) {
+  if (dtype == DT_BF16) return oracle_bf16_to_f32(oracle_bf16_from_f64(v));
+  return oracle_f32_from_f64(v);
+}
+
 static void store_act(int dtype, void* p, int64_t i, double v) {
   if (dtype == DT_BF16) ((uint16_t*)p)[i] = oracle_bf16_from_f64(v);
   else ((float*)p)[i] = oracle_f32_from_f64(v);
@@ -691,7 +697,8 @@ int oracle_router_backward(int64_t T, int H, int E, int K, int dtype, const void
 
 /* Expert FFN backward for the n rows of one group (x rows, dY rows; w13 [2I,H],
  * w2 [H,I] of that expert):  a = x W1^T, u = x W3^T, h = silu(a) u (stored at the
- * act dtype as in the forward),
+ * act dtype as in the forward; a and u are also kept at the act dtype, and the
+ * backward works from those kept values),
  *   dh  = dY W2,                  da = dh u silu'(a),  du = dh silu(a)  -> [da|du] stored,
  *   dx  = [da|du] W13             (stored at the act dtype),
  *   dW2 = dY^T h,  dW13 = [da|du]^T x   (fp32).
@@ -716,8 +723,11 @@ static void ebwd_row_item(void* c, int64_t r) {
       dh += dec(dt, B->dy, r * H + m) * dec(dt, B->w2, (int64_t)m * I + n);
     double sg = 1.0 / (1.0 + exp(-a));
     store_act(dt, B->hs, r * I + n, a * sg * u);
-    store_act(dt, B->dau, r * 2 * I + n, dh * u * sg * (1.0 + a * (1.0 - sg)));
-    store_act(dt, B->dau, r * 2 * I + I + n, dh * a * sg);
+    /* the forward keeps a and u for the backward at the activation dtype */
+    const double ar = act_round(dt, a), ur = act_round(dt, u);
+    double sr = 1.0 / (1.0 + exp(-ar));
+    store_act(dt, B->dau, r * 2 * I + n, dh * ur * sr * (1.0 + ar * (1.0 - sr)));
+    store_act(dt, B->dau, r * 2 * I + I + n, dh * ar * sr);
   }
   for (int k = 0; k < H; ++k) {
     double acc = 0.0;

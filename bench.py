@@ -11,7 +11,13 @@ Prints ONE JSON line: throughput (tokens/s), the roofline of the dominant kernel
 (the gate/up grouped GEMM, timed with HIP events on its launch stream) and the CPU
 oracle timed on a bounded sample of the same workload.
 
-  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload v3-bf16]
+--train times a training step of the layer instead: the forward keeping the gate/up
+pre-activations (moe_expert_ffn_up_save), the bias update, then the backward
+(moe_combine_backward -> moe_router_backward -> moe_expert_ffn_backward_input ->
+moe_expert_ffn_backward_weight -> moe_unpermute_sum) for a seeded output gradient.
+Its roofline is that of the weight-gradient GEMMs (fp32 gradient writes).
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload v3-bf16] [--train]
 """
 from __future__ import annotations
 
@@ -27,6 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s (7168d, 256e top-8, T=4096); MFMA % and HBM % of peak"
+METRIC_TRAIN = ("MoE-layer training-step tokens/s (forward + bias update + backward; 7168d, "
+                "256e top-8, T=4096)")
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}  # dense TFLOP/s
 VALU_FP32_PEAK = 78.6  # TFLOP/s: 256 CUs x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (no packed fp32)
@@ -36,10 +44,14 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha(expert):
-    """sha256 over the sources that define the gate/up GEMM of this expert dtype."""
+def kernel_source_sha(expert, train=False):
+    """sha256 over the sources that define the measured kernel: the gate/up GEMM of this
+    expert dtype, or (train) the weight-gradient GEMM."""
     csrc = os.path.join(ROOT, "mixture_experts_layer_added_amd", "csrc")
-    files = ["gemm_fp8.hip" if expert == "e4m3" else "gemm.hip", "common.h"]
+    if train:
+        files = ["gemm_bwd.hip", "common.h"]
+    else:
+        files = ["gemm_fp8.hip" if expert == "e4m3" else "gemm.hip", "common.h"]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
@@ -47,11 +59,13 @@ def kernel_source_sha(expert):
     return h.hexdigest()
 
 
-def measured_traffic(workload, expert, dispatch):
-    """HBM bytes per gate/up launch from the committed FETCH_SIZE / WRITE_SIZE counter
-    summary of this workload, or None when there is none or the kernel source has changed
-    since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"ffn_up_{workload}_hbm_traffic.md")
+def measured_traffic(workload, expert, dispatch, train=False):
+    """HBM bytes per launch of the measured kernel (gate/up GEMM, or with train the
+    weight-gradient GEMM) from the committed FETCH_SIZE / WRITE_SIZE counter summary of
+    this workload, or None when there is none or the kernel source has changed since
+    the counters were taken."""
+    kind = "ffn_bwd_weight" if train else "ffn_up"
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_hbm_traffic.md")
     if not os.path.exists(path):
         return None, "no counter summary"
     with open(path) as fh:
@@ -59,7 +73,7 @@ def measured_traffic(workload, expert, dispatch):
     if not m:
         return None, "counter summary unreadable"
     rec = json.loads(m.group(1))
-    if rec.get("source_sha256") != kernel_source_sha(expert):
+    if rec.get("source_sha256") != kernel_source_sha(expert, train):
         return None, "kernel changed since the counters were taken"
     if rec.get("dispatch") != dispatch:
         return None, f"counters were taken with dispatch '{rec.get('dispatch')}'"
@@ -77,8 +91,11 @@ def parse():
     ap.add_argument("--materialize", action="store_true",
                     help="permute writes x_sorted and the gate/up GEMM reads it (default: the "
                          "GEMM gathers its rows from x)")
-    ap.add_argument("--cpu-ffn-rows", type=int, default=2048,
-                    help="expert-FFN rows the oracle computes for its sample")
+    ap.add_argument("--train", action="store_true",
+                    help="time forward + bias update + backward (bf16 / fp32 experts)")
+    ap.add_argument("--cpu-ffn-rows", type=int, default=0,
+                    help="expert-FFN rows the oracle computes for its sample "
+                         "(default 2048; 256 with --train)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this size (for counter calibration)")
     return ap.parse_args()
@@ -122,33 +139,31 @@ def main():
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
     shape = Shape(T=w.T, H=w.H, E=w.E, G=w.G, M=w.M, K=w.K, J=w.J, I=w.I, S=w.S, act=w.act,
                   expert=w.expert)
+    if args.train and w.expert == "e4m3":
+        raise SystemExit("--train: the backward is built for the bf16 and fp32 expert paths")
     layer = MoELayer(shape, w_router, bias, w13, w2, s13, s2, device=dev,
-                     gather=not args.materialize)
+                     gather=not args.materialize, train=args.train)
+    dy = workloads.make_dy(w, device=dev) if args.train else None
     stream = torch.cuda.current_stream()
 
-    names = ["route", "permute", "ffn_up", "ffn_down", "combine", "bias_update"]
+    calls = [("route", lambda: layer.route(x)), ("permute", lambda: layer.permute(x)),
+             ("ffn_up", layer.expert_ffn_up), ("ffn_down", layer.expert_ffn_down),
+             ("combine", layer.combine), ("bias_update", lambda: layer.bias_step(w.gamma))]
+    if args.train:
+        calls += [("combine_bwd", lambda: layer.combine_backward(dy)),
+                  ("router_bwd", layer.router_backward),
+                  ("ffn_bwd_input", layer.expert_ffn_backward_input),
+                  ("ffn_bwd_weight", layer.expert_ffn_backward_weight),
+                  ("unpermute_sum", layer.unpermute_sum)]
+    names = [n for n, _ in calls]
 
     def step(ev=None):
+        for i, (_, call) in enumerate(calls):
+            if ev is not None:
+                ev[i].record(stream)
+            call()
         if ev is not None:
-            ev[0].record(stream)
-        layer.route(x)
-        if ev is not None:
-            ev[1].record(stream)
-        layer.permute(x)
-        if ev is not None:
-            ev[2].record(stream)
-        layer.expert_ffn_up()
-        if ev is not None:
-            ev[3].record(stream)
-        layer.expert_ffn_down()
-        if ev is not None:
-            ev[4].record(stream)
-        layer.combine()
-        if ev is not None:
-            ev[5].record(stream)
-        layer.bias_step(w.gamma)
-        if ev is not None:
-            ev[6].record(stream)
+            ev[len(calls)].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -167,7 +182,7 @@ def main():
     # event records do not perturb the timed region above)
     per = {n: [] for n in names}
     for _ in range(args.steps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
         step(ev)
         torch.cuda.synchronize()
         for i, n in enumerate(names):
@@ -185,6 +200,8 @@ def main():
     up_scales = touched * (2 * w.I // 128) * (w.H // 128) * 4 if w.expert == "e4m3" else 0
     up_act = R * w.H * es + R * w.I * es + (R * (w.H // 128 + w.I // 128) * 4 if es == 1 else 0)
     up_bytes = up_w + up_scales + up_act
+    if args.train:  # the gate/up pre-activations kept for the backward
+        up_bytes += R * 2 * w.I * act_es
     up_flops = 2.0 * R * 2 * w.I * w.H
     down_w = touched * w.H * w.I * es
     down_bytes = down_w + R * w.I * es + R * w.H * act_es
@@ -222,18 +239,53 @@ def main():
                     "hbm_frac": gbs(comb_bytes, avg_ms["combine"]) / HBM_PEAK_GBS},
         "bias_update": {"ms": avg_ms["bias_update"]},
     }
-    up_gbs = gbs(up_bytes, avg_ms["ffn_up"])
-    roofline = {"kernel": "k_gemm_bf16<true> (gate/up grouped GEMM + SwiGLU)"
-                if w.expert == "bf16" else f"gate/up grouped GEMM ({w.expert})",
-                "bound": "hbm", "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(up_gbs / HBM_PEAK_GBS, 4),
-                "bytes_per_launch": up_bytes, "ms_per_launch": round(avg_ms["ffn_up"], 4),
-                "traffic": None}
+    if args.train:
+        a, T, H, I, K, E = act_es, w.T, w.H, w.I, w.K, w.E
+        NG = E + w.S
+        cb_bytes = T * H * a + T * K * H * a + R * H * a + T * K * 12
+        rb_bytes = T * K * 12 + 2 * E * H * 4 + T * H * 4 + T * K * H * a
+        bi_bytes = (R * H * a + touched * H * I * es + R * 2 * I * a * 2
+                    + touched * 2 * I * H * es + R * H * a)
+        bi_flops = 2.0 * R * H * I + 2.0 * R * 2 * I * H
+        x_rows = R if args.materialize else T
+        # per launch: dW2 (dY, h in; NG x H x I fp32 out), dW13 (dau, x in; NG x 2I x H out)
+        bw_bytes = (R * H * a + R * I * a + NG * H * I * 4
+                    + R * 2 * I * a + x_rows * H * a + NG * 2 * I * H * 4)
+        bw_flops = 2.0 * R * H * I + 2.0 * R * 2 * I * H
+        us_bytes = R * H * a + T * H * 4 + T * H * a + T * K * 4
+        for n, b, f in (("combine_bwd", cb_bytes, 0), ("router_bwd", rb_bytes, 0),
+                        ("ffn_bwd_input", bi_bytes, bi_flops),
+                        ("ffn_bwd_weight", bw_bytes, bw_flops), ("unpermute_sum", us_bytes, 0)):
+            k = {"ms": avg_ms[n], "GB/s": gbs(b, avg_ms[n]),
+                 "hbm_frac": gbs(b, avg_ms[n]) / HBM_PEAK_GBS}
+            if f:
+                k["TFLOP/s"] = tfs(f, avg_ms[n])
+                k["mfma_frac"] = tfs(f, avg_ms[n]) / MFMA_PEAK[w.expert]
+            kernels[n] = k
+    if args.train:
+        # the weight-gradient call: two launches of k_gemm_tn_bf16 (dW2, then dW13);
+        # per-launch figures are the averages over the two
+        per_launch_ms = avg_ms["ffn_bwd_weight"] / 2
+        wg_gbs = gbs(bw_bytes / 2, per_launch_ms)
+        roofline = {"kernel": "k_gemm_tn_bf16 (expert weight gradients, fp32 out; 2 launches)"
+                    if w.expert == "bf16" else "k_tn_f32 (expert weight gradients)",
+                    "bound": "hbm", "achieved": round(wg_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(wg_gbs / HBM_PEAK_GBS, 4),
+                    "bytes_per_launch": bw_bytes // 2, "ms_per_launch": round(per_launch_ms, 4),
+                    "traffic": None}
+    else:
+        up_gbs = gbs(up_bytes, avg_ms["ffn_up"])
+        roofline = {"kernel": "k_gemm_bf16<true> (gate/up grouped GEMM + SwiGLU)"
+                    if w.expert == "bf16" else f"gate/up grouped GEMM ({w.expert})",
+                    "bound": "hbm", "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(up_gbs / HBM_PEAK_GBS, 4),
+                    "bytes_per_launch": up_bytes, "ms_per_launch": round(avg_ms["ffn_up"], 4),
+                    "traffic": None}
     dispatch = "materialized x_sorted" if args.materialize else "gather from x"
-    traffic, src = measured_traffic(w.name, w.expert, dispatch)
+    traffic, src = measured_traffic(w.name, w.expert, dispatch, args.train)
     roofline["traffic"] = traffic
     roofline["traffic_source"] = src
-    roofline["kernel_source_sha256"] = kernel_source_sha(w.expert)
+    roofline["kernel_source_sha256"] = kernel_source_sha(w.expert, args.train)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20)
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -244,18 +296,20 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
+        ffn_rows = args.cpu_ffn_rows or (256 if args.train else 2048)
         cpu = cpu_baseline(w, layer, x, w_router, bias,
                            w13 if w.expert != "e4m3" else (w13, s13, w2, s2), w2,
-                           args.cpu_ffn_rows)
+                           ffn_rows, dy if args.train else None)
 
     out = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC_TRAIN if args.train else METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.expert, "data": "synthetic (seeded; weights N(0,0.006), x N(0,1))",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "G": w.G, "M": w.M,
                    "K": w.K, "J": w.J, "I": w.I, "S": w.S, "act": w.act, "expert": w.expert,
-                   "dispatch": dispatch,
+                   "dispatch": dispatch, "step": "forward + bias update + backward"
+                   if args.train else "forward + bias update",
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -265,15 +319,14 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(w, layer, x, w_router, bias, w13, w2, ffn_rows):
+def cpu_baseline(w, layer, x, w_router, bias, w13, w2, ffn_rows, dy=None):
     """The CPU oracle on a bounded sample of the same workload: routing, permutation,
     combine and bias update of the whole batch, and the expert FFN on `ffn_rows`
-    rows (half from the first routed expert, half from the shared expert), whose
-    per-row time is scaled to the T*(K+1) rows of the batch."""
-    import concurrent.futures as cf
-
+    rows (half from the first routed experts, half from the shared expert), whose
+    per-row time is scaled to the T*(K+1) rows of the batch.  With dy (training step)
+    also the combine, router and unpermute backward of the whole batch and the expert
+    backward of the same sample rows, scaled the same way."""
     import numpy as np
-    import torch
 
     import oracle
     import workloads
@@ -285,7 +338,8 @@ def cpu_baseline(w, layer, x, w_router, bias, w13, w2, ffn_rows):
     fp8 = w.expert == "e4m3"
     log(f"[bench] cpu baseline: oracle on {threads} threads")
     t = time.perf_counter()
-    idx, gate, counts, _ = oracle.route(xn, wr, bn, w.G, w.M, w.K, w.J, nthreads=threads)
+    idx, gate, counts, z = oracle.route(xn, wr, bn, w.G, w.M, w.K, w.J, nthreads=threads,
+                                        want_logits=dy is not None)
     t_route = time.perf_counter() - t
     t = time.perf_counter()
     off, st, inv, xs, xsc = oracle.permute(xn, idx, counts, w.E, w.S,
@@ -336,11 +390,32 @@ def cpu_baseline(w, layer, x, w_router, bias, w13, w2, ffn_rows):
     measured = t_route + t_perm + t_ffn_sample + t_comb + t_bias
     log(f"[bench] cpu baseline: route {t_route:.2f}s permute {t_perm:.2f}s ffn sample "
         f"{t_ffn_sample:.2f}s ({n_rows} rows) combine {t_comb:.2f}s")
+    what = (f"route+permute+combine+bias of all {w.T} tokens; expert FFN on {n_rows} rows "
+            f"({experts})")
+    if dy is not None:
+        dyn = workloads.to_numpy(dy)
+        t = time.perf_counter()
+        dys, dg = oracle.combine_backward(dyn, ys, inv, gate, w.S, nthreads=threads)
+        dz, dxr, _ = oracle.router_backward(xn, wr, z, idx, gate, dg, nthreads=threads)
+        t_bwd_rest = time.perf_counter() - t
+        t_eb_sample = 0.0
+        for g, rows in sample:
+            a, b = workloads.to_numpy(w13[g]), workloads.to_numpy(w2[g])
+            t = time.perf_counter()
+            oracle.expert_backward(xs[rows], a, b, dys[rows], nthreads=threads)
+            t_eb_sample += time.perf_counter() - t
+        t = time.perf_counter()
+        oracle.unpermute_sum(ys, inv, dxr, w.T, w.S, nthreads=threads)
+        t_bwd_rest += time.perf_counter() - t
+        total += t_bwd_rest + t_eb_sample * (w.R / n_rows)
+        measured += t_bwd_rest + t_eb_sample
+        log(f"[bench] cpu baseline: backward (combine, router, unpermute) {t_bwd_rest:.2f}s, "
+            f"expert backward sample {t_eb_sample:.2f}s")
+        what = (f"forward, bias update and combine/router/unpermute backward of all {w.T} "
+                f"tokens; expert FFN forward and backward on {n_rows} rows ({experts})")
     return {"value": round(w.T / total, 3), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": (f"route+permute+combine+bias of all {w.T} tokens; expert FFN on "
-                       f"{n_rows} rows ({experts}) scaled to the "
-                       f"{w.R} rows of the batch; {measured:.1f}s measured"),
+            "sample": (f"{what} scaled to the {w.R} rows of the batch; {measured:.1f}s measured"),
             "seconds_per_step_extrapolated": round(total, 2)}
 
 

@@ -206,6 +206,83 @@ moe_status moe_combine(const moe_problem* p, const void* y_sorted, const int32_t
 moe_status moe_bias_update(const moe_problem* p, const int32_t* expert_counts, float gamma,
                            float* bias, void* stream);
 
+/* ---------------- backward of the layer (bf16 and fp32 paths) ----------------
+ * The derivative of the forward above.  The pages fix only that the routing bias
+ * takes no part in back-propagation (blog.resmic.cn section 核心架构三) and that
+ * gradients accumulate at high precision (joto.ai item 3, FP32 accumulation): all
+ * reductions are fp32, weight gradients are stored in fp32, the bias has no gradient.
+ * One backward step, after a forward whose gate/up GEMM ran as moe_expert_ffn_up_save:
+ *   moe_combine_backward -> moe_router_backward -> moe_expert_ffn_backward_input
+ *   -> moe_expert_ffn_backward_weight -> moe_unpermute_sum.
+ * The expert backward comes in two calls, input gradient and weight gradient, as the
+ * pages' pipeline schedule splits a backward block (mpbf.cn section 3.2, DualPipe):
+ * the weight part has no consumer inside the layer and may run later or elsewhere.
+ * FP8 expert dtype: MOE_ERR_UNSUPPORTED. */
+
+/* moe_expert_ffn_up (or _gather) that also keeps the gate and up pre-activations for
+ * the backward:  au [R, 2I] act_dtype out, au[r][n] = a = x W13[g][n],
+ * au[r][I + n] = u = x W13[g][I + n] (fp32 sums rounded to act_dtype).  h as
+ * moe_expert_ffn_up.  sorted_token == NULL: x is x_sorted [R,H]; else x is [T,H] and
+ * row r is x[sorted_token[r]] (limit as moe_expert_ffn_up_gather). */
+moe_status moe_expert_ffn_up_save(const moe_problem* p, const void* x,
+                                  const int32_t* sorted_token, const int32_t* offsets,
+                                  const void* w13, void* h, void* au, void* stream);
+
+/* Combine backward (of moe_combine):
+ *   dy_sorted[inv_perm[t,k]] = topk_gate[t,k] * dy[t]  (rounded to act_dtype),
+ *   dy_sorted[T*K + t]       = dy[t]                   (shared expert, S = 1),
+ *   dgate[t,k]               = sum_h dy[t,h] * y_sorted[inv_perm[t,k], h]  (fp32).
+ *   dy [T,H] act; y_sorted [R,H] act (the forward's); inv_perm, topk_gate [T,K];
+ *   dy_sorted [R,H] act out; dgate [T,K] fp32 out. */
+moe_status moe_combine_backward(const moe_problem* p, const void* dy, const void* y_sorted,
+                                const int32_t* inv_perm, const float* topk_gate,
+                                void* dy_sorted, float* dgate, void* stream);
+
+/* Gate and router backward (mpbf.cn section 2.2: gates are the chosen sigmoid
+ * affinities renormalised; the bias only chose them):  with s = sigmoid(clamp(z,+-80))
+ * of the chosen experts and S their sum,
+ *   dz[t,j] = (dgate[t,j] - sum_k gate[t,k] dgate[t,k]) / S * s_j (1 - s_j)
+ *             (0 where |z| > 80),
+ *   dx_router[t] = sum_j dz[t,j] W_r[e_j]            [T,H] fp32 out,
+ *   dw_router[e] = sum over the rows of expert e, tokens ascending, of dz x[token]
+ *                                                      [E,H] fp32 out.
+ *   logits [T,E] fp32 from moe_route (logits_out); offsets, sorted_token from
+ *   moe_permute; dz [T,K] fp32 out. */
+moe_status moe_router_backward(const moe_problem* p, const void* x, const float* w_router,
+                               const float* logits, const int32_t* topk_idx,
+                               const float* topk_gate, const float* dgate,
+                               const int32_t* offsets, const int32_t* sorted_token, float* dz,
+                               float* dx_router, float* dw_router, void* stream);
+
+/* Expert FFN backward, input part, per group g over its rows (grouped GEMMs, fp32
+ * accumulation):
+ *   dh = dY W2[g];  da = dh u silu'(a), du = dh silu(a)  -> dau [R,2I] act out;
+ *   dx_sorted = dau W13[g]                               -> [R,H] act out.
+ *   au from moe_expert_ffn_up_save; dy_sorted [R,H] act from moe_combine_backward.
+ * Extra limit (checked): R*max(H,2I)*(bytes per element) < 2^31 - 16. */
+moe_status moe_expert_ffn_backward_input(const moe_problem* p, const int32_t* offsets,
+                                         const void* w13, const void* w2, const void* au,
+                                         const void* dy_sorted, void* dau, void* dx_sorted,
+                                         void* stream);
+
+/* Expert FFN backward, weight part, per group g over its rows (fp32 accumulation):
+ *   dw2[g]  = dY^T h    [E+S,H,I]  fp32 out,
+ *   dw13[g] = dau^T x   [E+S,2I,H] fp32 out   (groups without rows get zeros).
+ *   x: x_sorted [R,H] (sorted_token NULL) or x [T,H] with sorted_token; h from
+ *   moe_expert_ffn_up_save; dy_sorted from moe_combine_backward; dau from
+ *   moe_expert_ffn_backward_input.  Same extra limit as the input part. */
+moe_status moe_expert_ffn_backward_weight(const moe_problem* p, const void* x,
+                                          const int32_t* sorted_token, const int32_t* offsets,
+                                          const void* h, const void* dy_sorted, const void* dau,
+                                          float* dw13, float* dw2, void* stream);
+
+/* Input gradient: dx[t] = dx_router[t] + sum_k dx_sorted[inv_perm[t,k]] + dx_sorted[T*K+t]
+ * (last term if S = 1), summed in fp32 in that order, rounded to act_dtype.
+ * dx_router may be NULL (then omitted). */
+moe_status moe_unpermute_sum(const moe_problem* p, const void* dx_sorted,
+                             const int32_t* inv_perm, const float* dx_router, void* dx,
+                             void* stream);
+
 /* Offline FP8 preparation of expert weights (mpbf.cn section 4.3: block-wise scaling
  * instead of one global scale): for `batch` bf16 matrices [rows, cols] (rows and cols
  * multiples of 128) write E4M3 codes [batch, rows, cols] and fp32 scales

@@ -20,7 +20,9 @@ MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_EXPERT_FFN = 0, 1, 2
 EXPORTS = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_up",
            "moe_expert_ffn_up_gather", "moe_quantize_act_fp8", "moe_expert_ffn_down",
            "moe_combine", "moe_bias_update", "moe_quantize_weights_fp8", "moe_workspace_bytes",
-           "moe_status_str", "moe_last_error")
+           "moe_status_str", "moe_last_error", "moe_expert_ffn_up_save", "moe_combine_backward",
+           "moe_router_backward", "moe_expert_ffn_backward_input",
+           "moe_expert_ffn_backward_weight", "moe_unpermute_sum")
 
 
 class MoeError(RuntimeError):
@@ -60,6 +62,12 @@ def lib():
         L.moe_expert_ffn_up.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_expert_ffn_up_gather.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_quantize_act_fp8.argtypes = [pp, vp, vp, vp, vp]
+        L.moe_expert_ffn_up_save.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_combine_backward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_router_backward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_expert_ffn_backward_input.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_expert_ffn_backward_weight.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_unpermute_sum.argtypes = [pp, vp, vp, vp, vp, vp]
         L.moe_expert_ffn_down.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_combine.argtypes = [pp, vp, vp, vp, vp, vp]
         L.moe_bias_update.argtypes = [pp, vp, f32, vp, vp]
@@ -72,7 +80,10 @@ def lib():
         L.moe_last_error.restype = ctypes.c_char_p
         for n in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_up",
                   "moe_expert_ffn_up_gather", "moe_quantize_act_fp8", "moe_expert_ffn_down",
-                  "moe_combine", "moe_bias_update", "moe_quantize_weights_fp8"):
+                  "moe_combine", "moe_bias_update", "moe_quantize_weights_fp8",
+                  "moe_expert_ffn_up_save", "moe_combine_backward", "moe_router_backward",
+                  "moe_expert_ffn_backward_input", "moe_expert_ffn_backward_weight",
+                  "moe_unpermute_sum"):
             getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -174,3 +185,48 @@ def moe_bias_update(p, expert_counts, gamma, bias, stream=None):
 def moe_quantize_weights_fp8(w_bf16, w_fp8, scale, batch, rows, cols, stream=None):
     _check(lib().moe_quantize_weights_fp8(_ptr(w_bf16), _ptr(w_fp8), _ptr(scale), batch, rows,
                                           cols, _stream(stream)), "moe_quantize_weights_fp8")
+
+
+
+def moe_expert_ffn_up_save(p, x, sorted_token, offsets, w13, h, au, stream=None):
+    _check(lib().moe_expert_ffn_up_save(ctypes.byref(p), _ptr(x), _ptr(sorted_token),
+                                        _ptr(offsets), _ptr(w13), _ptr(h), _ptr(au),
+                                        _stream(stream)), "moe_expert_ffn_up_save")
+
+
+def moe_combine_backward(p, dy, y_sorted, inv_perm, topk_gate, dy_sorted, dgate, stream=None):
+    _check(lib().moe_combine_backward(ctypes.byref(p), _ptr(dy), _ptr(y_sorted), _ptr(inv_perm),
+                                      _ptr(topk_gate), _ptr(dy_sorted), _ptr(dgate),
+                                      _stream(stream)), "moe_combine_backward")
+
+
+def moe_router_backward(p, x, w_router, logits, topk_idx, topk_gate, dgate, offsets,
+                        sorted_token, dz, dx_router, dw_router, stream=None):
+    _check(lib().moe_router_backward(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(logits),
+                                     _ptr(topk_idx), _ptr(topk_gate), _ptr(dgate),
+                                     _ptr(offsets), _ptr(sorted_token), _ptr(dz),
+                                     _ptr(dx_router), _ptr(dw_router), _stream(stream)),
+           "moe_router_backward")
+
+
+def moe_expert_ffn_backward_input(p, offsets, w13, w2, au, dy_sorted, dau, dx_sorted,
+                                  stream=None):
+    _check(lib().moe_expert_ffn_backward_input(ctypes.byref(p), _ptr(offsets), _ptr(w13),
+                                               _ptr(w2), _ptr(au), _ptr(dy_sorted), _ptr(dau),
+                                               _ptr(dx_sorted), _stream(stream)),
+           "moe_expert_ffn_backward_input")
+
+
+def moe_expert_ffn_backward_weight(p, x, sorted_token, offsets, h, dy_sorted, dau, dw13, dw2,
+                                   stream=None):
+    _check(lib().moe_expert_ffn_backward_weight(ctypes.byref(p), _ptr(x), _ptr(sorted_token),
+                                                _ptr(offsets), _ptr(h), _ptr(dy_sorted),
+                                                _ptr(dau), _ptr(dw13), _ptr(dw2),
+                                                _stream(stream)),
+           "moe_expert_ffn_backward_weight")
+
+
+def moe_unpermute_sum(p, dx_sorted, inv_perm, dx_router, dx, stream=None):
+    _check(lib().moe_unpermute_sum(ctypes.byref(p), _ptr(dx_sorted), _ptr(inv_perm),
+                                   _ptr(dx_router), _ptr(dx), _stream(stream)),
+           "moe_unpermute_sum")

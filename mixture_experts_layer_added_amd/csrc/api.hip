@@ -315,6 +315,149 @@ moe_status moe_bias_update(const moe_problem* p, const int32_t* expert_counts, f
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_bias_update launch");
 }
 
+static moe_status require_no_fp8(const Dims& d, const char* call) {
+  if (d.expert == MOE_FP8_E4M3)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: the backward is built for the bf16 and fp32 paths", call);
+  return MOE_OK;
+}
+
+moe_status moe_combine_backward(const moe_problem* p, const void* dy, const void* y_sorted,
+                                const int32_t* inv_perm, const float* topk_gate, void* dy_sorted,
+                                float* dgate, void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  if ((s = require_no_fp8(d, "moe_combine_backward")) != MOE_OK) return s;
+  REQUIRE_PTR(dy);
+  REQUIRE_PTR(y_sorted);
+  REQUIRE_PTR(dy_sorted);
+  if (!inv_perm || !topk_gate || !dgate)
+    return fail(MOE_ERR_INVALID_ARG, "inv_perm, topk_gate and dgate are required");
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  hipError_t e = launch_combine_bwd(d, dy, y_sorted, inv_perm, topk_gate, dy_sorted, dgate,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_combine_backward launch");
+}
+
+moe_status moe_router_backward(const moe_problem* p, const void* x, const float* w_router,
+                               const float* logits, const int32_t* topk_idx,
+                               const float* topk_gate, const float* dgate,
+                               const int32_t* offsets, const int32_t* sorted_token, float* dz,
+                               float* dx_router, float* dw_router, void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  if ((s = require_no_fp8(d, "moe_router_backward")) != MOE_OK) return s;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_router);
+  REQUIRE_PTR(dx_router);
+  REQUIRE_PTR(dw_router);
+  if (!logits || !topk_idx || !topk_gate || !dgate || !offsets || !sorted_token || !dz)
+    return fail(MOE_ERR_INVALID_ARG,
+                "logits, topk_idx, topk_gate, dgate, offsets, sorted_token and dz are required");
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  hipError_t e = launch_router_bwd(d, x, w_router, logits, topk_idx, topk_gate, dgate, offsets,
+                                   sorted_token, dz, dx_router, dw_router,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_router_backward launch");
+}
+
+moe_status moe_unpermute_sum(const moe_problem* p, const void* dx_sorted,
+                             const int32_t* inv_perm, const float* dx_router, void* dx,
+                             void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  if ((s = require_no_fp8(d, "moe_unpermute_sum")) != MOE_OK) return s;
+  REQUIRE_PTR(dx_sorted);
+  REQUIRE_PTR(dx);
+  if (dx_router && !aligned16(dx_router))
+    return fail(MOE_ERR_INVALID_ARG, "dx_router is not 16-byte aligned");
+  if (!inv_perm) return fail(MOE_ERR_INVALID_ARG, "inv_perm is NULL");
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  hipError_t e = launch_unpermute_sum(d, dx_sorted, inv_perm, dx_router, dx,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_unpermute_sum launch");
+}
+
+moe_status moe_expert_ffn_up_save(const moe_problem* p, const void* x,
+                                  const int32_t* sorted_token, const int32_t* offsets,
+                                  const void* w13, void* h, void* au, void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  if ((s = require_no_fp8(d, "moe_expert_ffn_up_save")) != MOE_OK) return s;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w13);
+  REQUIRE_PTR(h);
+  REQUIRE_PTR(au);
+  if (!offsets) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL");
+  const int es = d.expert == MOE_F32 ? 4 : 2;
+  if (sorted_token && d.T * (int64_t)d.H * es >= ((int64_t)1 << 31) - 16)
+    return fail(MOE_ERR_INVALID_ARG, "T*H*%d must be < 2^31 - 16 (32-bit row offsets)", es);
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  hipError_t e = launch_ffn_up(d, x, nullptr, offsets, sorted_token, w13, nullptr, h, nullptr,
+                               static_cast<hipStream_t>(stream), au);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn_up_save launch");
+}
+
+static moe_status check_bwd_rows(const Dims& d) {
+  const int es = d.expert == MOE_F32 ? 4 : 2;
+  const int64_t widest = d.H > 2 * d.I ? d.H : 2 * d.I;
+  if (d.R() * widest * es >= ((int64_t)1 << 31) - 16)
+    return fail(MOE_ERR_INVALID_ARG,
+                "R*max(H,2I)*%d must be < 2^31 - 16 (32-bit row offsets in the backward)", es);
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn_backward_input(const moe_problem* p, const int32_t* offsets,
+                                         const void* w13, const void* w2, const void* au,
+                                         const void* dy_sorted, void* dau, void* dx_sorted,
+                                         void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  if ((s = require_no_fp8(d, "moe_expert_ffn_backward_input")) != MOE_OK) return s;
+  REQUIRE_PTR(w13);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(au);
+  REQUIRE_PTR(dy_sorted);
+  REQUIRE_PTR(dau);
+  REQUIRE_PTR(dx_sorted);
+  if (!offsets) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL");
+  if ((s = check_bwd_rows(d)) != MOE_OK) return s;
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  hipError_t e = launch_ffn_bwd_input(d, offsets, w13, w2, au, dy_sorted, dau, dx_sorted,
+                                      static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported)
+    return fail(MOE_ERR_UNSUPPORTED, "no backward kernel for expert dtype %d", d.expert);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn_backward_input launch");
+}
+
+moe_status moe_expert_ffn_backward_weight(const moe_problem* p, const void* x,
+                                          const int32_t* sorted_token, const int32_t* offsets,
+                                          const void* h, const void* dy_sorted, const void* dau,
+                                          float* dw13, float* dw2, void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  if ((s = require_no_fp8(d, "moe_expert_ffn_backward_weight")) != MOE_OK) return s;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(h);
+  REQUIRE_PTR(dy_sorted);
+  REQUIRE_PTR(dau);
+  REQUIRE_PTR(dw13);
+  REQUIRE_PTR(dw2);
+  if (!offsets) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL");
+  if ((s = check_bwd_rows(d)) != MOE_OK) return s;
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  hipError_t e = launch_ffn_bwd_weight(d, x, sorted_token, offsets, h, dy_sorted, dau, dw13, dw2,
+                                       static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported)
+    return fail(MOE_ERR_UNSUPPORTED, "no backward kernel for expert dtype %d", d.expert);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn_backward_weight launch");
+}
+
 moe_status moe_quantize_weights_fp8(const void* w_bf16, void* w_fp8, float* scale,
                                     int64_t batch, int32_t rows, int32_t cols, void* stream) {
   if (batch < 1 || rows < 128 || cols < 128 || rows % 128 || cols % 128)

@@ -92,6 +92,36 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   return static_cast<uint32_t>(w);
 }
 
+// ---------------------------------------------------------------------------
+// exp and sigmoid of the router (shared by the routing and its backward).  ln 2 is split for Cody-Waite reduction: the high part is ln 2
+// rounded to 16 significant bits (45426/65536) so k*LN2_HI is exact for |k| < 256;
+// the low part is the float nearest ln 2 - LN2_HI.  The polynomial is the Taylor
+// series of exp to degree 7 with coefficients rounded to float (1/n!).  |a| <= 80
+// keeps k within [-116, 116] and 2^k a normal float, so the final scaling is exact.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float exp_cw7(float a) {
+  constexpr float kInvLn2 = 0x1.715476p+0f;
+  constexpr float kLn2Hi = 0x1.62e4p-1f;
+  constexpr float kLn2Lo = 0x1.7f7d1cp-20f;
+  const float k = __builtin_rintf(a * kInvLn2);
+  float r = __builtin_fmaf(-k, kLn2Hi, a);
+  r = __builtin_fmaf(-k, kLn2Lo, r);
+  float p = 0x1.a01a02p-13f;
+  p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);
+  p = __builtin_fmaf(p, r, 0x1.111112p-7f);
+  p = __builtin_fmaf(p, r, 0x1.555556p-5f);
+  p = __builtin_fmaf(p, r, 0x1.555556p-3f);
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  return p * __uint_as_float(static_cast<uint32_t>(static_cast<int>(k) + 127) << 23);
+}
+
+__device__ __forceinline__ float affinity(float z) {
+  const float zc = __builtin_fminf(__builtin_fmaxf(z, -80.0f), 80.0f);
+  return 1.0f / (1.0f + exp_cw7(-zc));
+}
+
 // ---- launchers (each returns hipGetLastError() of its launch) ----
 struct Dims {
   int64_t T;
@@ -114,9 +144,12 @@ size_t ffn_ws_bytes(const Dims& d);
 float* ffn_ws_h_scale(const Dims& d, void* ws);
 // gather: nullptr (xs is the permuted x_sorted) or sorted_token (xs is the unpermuted
 // input, [T, H], and row r of the permuted order is xs row gather[r])
+// au != nullptr (bf16 / fp32 paths): the gate and up pre-activations, [R, 2I] at the
+// activation dtype, are written as well (for the backward)
 hipError_t launch_ffn_up(const Dims& d, const void* xs, const float* xs_scale,
                          const int32_t* offsets, const int32_t* gather, const void* w13,
-                         const float* w13_scale, void* h, float* h_scale, hipStream_t st);
+                         const float* w13_scale, void* h, float* h_scale, hipStream_t st,
+                         void* au = nullptr);
 hipError_t launch_ffn_down(const Dims& d, const void* h, const float* h_scale,
                            const int32_t* offsets, const void* w2, const float* w2_scale, void* ys,
                            hipStream_t st);
@@ -137,6 +170,26 @@ hipError_t launch_bias_update(const Dims& d, const int32_t* counts, float gamma,
 
 hipError_t launch_quantize_weights(const uint16_t* w, uint8_t* q, float* scale, int64_t batch,
                                    int rows, int cols, hipStream_t st);
+
+// backward (backward.hip, gemm_bwd.hip)
+hipError_t launch_combine_bwd(const Dims& d, const void* dy, const void* ys,
+                              const int32_t* inv_perm, const float* gate, void* dys, float* dgate,
+                              hipStream_t st);
+hipError_t launch_router_bwd(const Dims& d, const void* x, const float* w, const float* z,
+                             const int32_t* idx, const float* gate, const float* dgate,
+                             const int32_t* offsets, const int32_t* sorted_token, float* dz,
+                             float* dxr, float* dw, hipStream_t st);
+hipError_t launch_unpermute_sum(const Dims& d, const void* dxs, const int32_t* inv_perm,
+                                const float* dxr, void* dx, hipStream_t st);
+// expert backward, input part: dys -> dau -> dxs
+hipError_t launch_ffn_bwd_input(const Dims& d, const int32_t* offsets, const void* w13,
+                                const void* w2, const void* au, const void* dys, void* dau,
+                                void* dxs, hipStream_t st);
+// expert backward, weight part; x: x_sorted (gather == nullptr) or x [T, H] read
+// through gather = sorted_token
+hipError_t launch_ffn_bwd_weight(const Dims& d, const void* x, const int32_t* gather,
+                                 const int32_t* offsets, const void* h, const void* dys,
+                                 const void* dau, float* dw13, float* dw2, hipStream_t st);
 
 int device_cu_count();
 

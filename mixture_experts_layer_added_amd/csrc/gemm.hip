@@ -38,7 +38,8 @@ template <bool kSwiglu>
 __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
                                                   const float* __restrict__ B, float* __restrict__ C,
                                                   const int32_t* __restrict__ offsets,
-                                                  const int32_t* __restrict__ gather, int NG,
+                                                  const int32_t* __restrict__ gather,
+                                                  float* __restrict__ au, int NG,
                                                   int Kd, int Nrows, int Nout, int half) {
   constexpr int BM = 64, BN = 64, BK = 16;
   __shared__ __attribute__((aligned(16))) float As[BK][BM];
@@ -98,8 +99,14 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
       float* cp = C + (int64_t)(row0 + m) * Nout;
       if (kSwiglu) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          cp[tl.n_idx * 32 + tx * 2 + j] = silu(acc[i][j]) * acc[i][2 + j];
+        for (int j = 0; j < 2; ++j) {
+          const int col = tl.n_idx * 32 + tx * 2 + j;
+          cp[col] = silu(acc[i][j]) * acc[i][2 + j];
+          if (au) {  // gate and up pre-activations, kept for the backward
+            au[(int64_t)(row0 + m) * 2 * half + col] = acc[i][j];
+            au[(int64_t)(row0 + m) * 2 * half + half + col] = acc[i][2 + j];
+          }
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) cp[tl.n_idx * BN + tx * 4 + j] = acc[i][j];
@@ -154,6 +161,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
                                                       uint16_t* __restrict__ C,
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ gather,
+                                                      uint16_t* __restrict__ au,
                                                       int a_rows, int NG, int Kd, int Nrows,
                                                       int Nout, int half) {
   __shared__ __attribute__((aligned(1024))) char smem[kRing];
@@ -294,9 +302,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
           uint16_t* cp = C + (int64_t)(row0 + m0 + m) * Nout;
           if (kSwiglu) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-              cp[tl.n_idx * 128 + 64 * wn + 32 * t + (lane & 31)] =
-                  f32_to_bf16_bits(silu(acc[mi][2 * t][i]) * acc[mi][2 * t + 1][i]);
+            for (int t = 0; t < 2; ++t) {
+              const int col = tl.n_idx * 128 + 64 * wn + 32 * t + (lane & 31);
+              cp[col] = f32_to_bf16_bits(silu(acc[mi][2 * t][i]) * acc[mi][2 * t + 1][i]);
+              if (au) {  // gate and up pre-activations, kept for the backward
+                uint16_t* ap = au + (int64_t)(row0 + m0 + m) * 2 * half;
+                ap[col] = f32_to_bf16_bits(acc[mi][2 * t][i]);
+                ap[half + col] = f32_to_bf16_bits(acc[mi][2 * t + 1][i]);
+              }
+            }
           } else {
 #pragma unroll
             for (int n = 0; n < 4; ++n)
@@ -330,20 +344,22 @@ float* ffn_ws_h_scale(const Dims& d, void* ws) {
 
 hipError_t launch_ffn_up(const Dims& d, const void* xs, const float* xs_scale,
                          const int32_t* offsets, const int32_t* gather, const void* w13,
-                         const float* w13_scale, void* h, float* h_scale, hipStream_t st) {
+                         const float* w13_scale, void* h, float* h_scale, hipStream_t st,
+                         void* au) {
   const int NG = d.E + d.S;
   const int cus = device_cu_count();
   if (d.expert == MOE_F32) {
     hipLaunchKernelGGL(k_gemm_f32<true>, dim3(persistent_grid(cus, 4)), dim3(256), 0, st,
                        static_cast<const float*>(xs), static_cast<const float*>(w13),
-                       static_cast<float*>(h), offsets, gather, NG, d.H, 2 * d.I, d.I, d.I);
+                       static_cast<float*>(h), offsets, gather, static_cast<float*>(au), NG, d.H,
+                       2 * d.I, d.I, d.I);
     return hipGetLastError();
   }
   if (d.expert == MOE_BF16) {
     hipLaunchKernelGGL(k_gemm_bf16<true>, dim3(persistent_grid(cus, 1)), dim3(512), 0, st,
                        static_cast<const uint16_t*>(xs), static_cast<const uint16_t*>(w13),
-                       static_cast<uint16_t*>(h), offsets, gather, (int)d.T, NG, d.H, 2 * d.I,
-                       d.I, d.I);
+                       static_cast<uint16_t*>(h), offsets, gather, static_cast<uint16_t*>(au),
+                       (int)d.T, NG, d.H, 2 * d.I, d.I, d.I);
     return hipGetLastError();
   }
   return launch_fp8_up(d, xs, xs_scale, offsets, gather, w13, w13_scale, h, h_scale, st);
@@ -357,13 +373,14 @@ hipError_t launch_ffn_down(const Dims& d, const void* h, const float* h_scale,
   if (d.expert == MOE_F32) {
     hipLaunchKernelGGL(k_gemm_f32<false>, dim3(persistent_grid(cus, 4)), dim3(256), 0, st,
                        static_cast<const float*>(h), static_cast<const float*>(w2),
-                       static_cast<float*>(ys), offsets, nullptr, NG, d.I, d.H, d.H, 0);
+                       static_cast<float*>(ys), offsets, nullptr, nullptr, NG, d.I, d.H, d.H, 0);
     return hipGetLastError();
   }
   if (d.expert == MOE_BF16) {
     hipLaunchKernelGGL(k_gemm_bf16<false>, dim3(persistent_grid(cus, 1)), dim3(512), 0, st,
                        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w2),
-                       static_cast<uint16_t*>(ys), offsets, nullptr, 0, NG, d.I, d.H, d.H, 0);
+                       static_cast<uint16_t*>(ys), offsets, nullptr, nullptr, 0, NG, d.I, d.H, d.H,
+                       0);
     return hipGetLastError();
   }
   return launch_fp8_down(d, h, h_scale, offsets, w2, w2_scale, ys, st);

@@ -135,36 +135,6 @@ __global__ __launch_bounds__(RWV * kWave) void k_router_logits(const XT* __restr
       if (eb + e < E) z[(int64_t)t * E + eb + e] = acc[e];
 }
 
-// ---------------------------------------------------------------------------
-// exp and sigmoid.  ln 2 is split for Cody-Waite reduction: the high part is ln 2
-// rounded to 16 significant bits (45426/65536) so k*LN2_HI is exact for |k| < 256;
-// the low part is the float nearest ln 2 - LN2_HI.  The polynomial is the Taylor
-// series of exp to degree 7 with coefficients rounded to float (1/n!).  |a| <= 80
-// keeps k within [-116, 116] and 2^k a normal float, so the final scaling is exact.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float exp_cw7(float a) {
-  constexpr float kInvLn2 = 0x1.715476p+0f;
-  constexpr float kLn2Hi = 0x1.62e4p-1f;
-  constexpr float kLn2Lo = 0x1.7f7d1cp-20f;
-  const float k = __builtin_rintf(a * kInvLn2);
-  float r = __builtin_fmaf(-k, kLn2Hi, a);
-  r = __builtin_fmaf(-k, kLn2Lo, r);
-  float p = 0x1.a01a02p-13f;
-  p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);
-  p = __builtin_fmaf(p, r, 0x1.111112p-7f);
-  p = __builtin_fmaf(p, r, 0x1.555556p-5f);
-  p = __builtin_fmaf(p, r, 0x1.555556p-3f);
-  p = __builtin_fmaf(p, r, 0.5f);
-  p = __builtin_fmaf(p, r, 1.0f);
-  p = __builtin_fmaf(p, r, 1.0f);
-  return p * __uint_as_float(static_cast<uint32_t>(static_cast<int>(k) + 127) << 23);
-}
-
-__device__ __forceinline__ float affinity(float z) {
-  const float zc = __builtin_fminf(__builtin_fmaxf(z, -80.0f), 80.0f);
-  return 1.0f / (1.0f + exp_cw7(-zc));
-}
-
 // (value, index) ordering: larger value first, then the lower index.
 __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);

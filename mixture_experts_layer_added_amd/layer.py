@@ -58,13 +58,17 @@ class MoELayer:
     gather=True:  permute writes the index maps only (FP8: plus one quantisation of x
     per token) and the gate/up GEMM reads its rows from x through sorted_token; the
     results are identical and the permuted copy of x is never written.
+    train=True (bf16 / fp32): the gate/up GEMM also keeps the pre-activations (au) and
+    backward(dy) computes dx, dw_router, dw13 and dw2 (weight gradients in fp32).
     """
 
     def __init__(self, shape: Shape, w_router, bias, w13, w2, w13_scale=None, w2_scale=None,
-                 device="cuda", gather=False):
+                 device="cuda", gather=False, train=False):
         self.shape = shape
         self.gather = gather
+        self.train = train
         self._x = None
+        self._xin = None
         self.p = shape.problem()
         self.w_router, self.bias = w_router, bias
         self.w13, self.w2, self.w13_scale, self.w2_scale = w13, w2, w13_scale, w2_scale
@@ -97,6 +101,20 @@ class MoELayer:
             self.h_scale = None
         self.y_sorted = torch.empty((R, H), dtype=act, device=dev)
         self.y = torch.empty((T, H), dtype=act, device=dev)
+        if train:
+            assert shape.expert != "e4m3", "the backward is built for the bf16 and fp32 paths"
+            NG, I, f32 = E + shape.S, shape.I, torch.float32
+            self.au = torch.empty((R, 2 * I), dtype=act, device=dev)
+            self.dy_sorted = torch.empty((R, H), dtype=act, device=dev)
+            self.dgate = torch.empty((T, K), dtype=f32, device=dev)
+            self.dz = torch.empty((T, K), dtype=f32, device=dev)
+            self.dx_router = torch.empty((T, H), dtype=f32, device=dev)
+            self.dw_router = torch.empty((E, H), dtype=f32, device=dev)
+            self.dau = torch.empty((R, 2 * I), dtype=act, device=dev)
+            self.dx_sorted = torch.empty((R, H), dtype=act, device=dev)
+            self.dw13 = torch.empty((NG, 2 * I, H), dtype=f32, device=dev)
+            self.dw2 = torch.empty((NG, H, I), dtype=f32, device=dev)
+            self.dx = torch.empty((T, H), dtype=act, device=dev)
         self.ws = {}
         for call in (L.MOE_CALL_ROUTE, L.MOE_CALL_PERMUTE):
             n = L.moe_workspace_bytes(self.p, call)
@@ -123,9 +141,14 @@ class MoELayer:
         else:
             L.moe_permute(self.p, x, self.topk_idx, self.offsets, self.sorted_token,
                           self.inv_perm, self.x_sorted, self.x_scale, ws, n, stream)
+            self._xin = x
 
     def expert_ffn_up(self, stream=None):
-        if self.gather:
+        if self.train:
+            xin, st = (self._x, self.sorted_token) if self.gather else (self.x_sorted, None)
+            L.moe_expert_ffn_up_save(self.p, xin, st, self.offsets, self.w13, self.h, self.au,
+                                     stream)
+        elif self.gather:
             xin = self.x_q if self.shape.expert == "e4m3" else self._x
             L.moe_expert_ffn_up_gather(self.p, xin, self.x_scale, self.sorted_token,
                                        self.offsets, self.w13, self.w13_scale, self.h,
@@ -157,6 +180,40 @@ class MoELayer:
     def bias_step(self, gamma=0.01, stream=None):
         """Aux-loss-free bias update from this batch's expert counts (in place)."""
         L.moe_bias_update(self.p, self.counts, gamma, self.bias, stream)
+
+    def expert_ffn_backward_input(self, stream=None):
+        L.moe_expert_ffn_backward_input(self.p, self.offsets, self.w13, self.w2, self.au,
+                                        self.dy_sorted, self.dau, self.dx_sorted, stream)
+
+    def expert_ffn_backward_weight(self, stream=None):
+        xin, st = (self._x, self.sorted_token) if self.gather else (self.x_sorted, None)
+        L.moe_expert_ffn_backward_weight(self.p, xin, st, self.offsets, self.h, self.dy_sorted,
+                                         self.dau, self.dw13, self.dw2, stream)
+
+    def combine_backward(self, dy, stream=None):
+        L.moe_combine_backward(self.p, dy, self.y_sorted, self.inv_perm, self.topk_gate,
+                               self.dy_sorted, self.dgate, stream)
+
+    def router_backward(self, stream=None):
+        x = self._x if self.gather else self._xin
+        L.moe_router_backward(self.p, x, self.w_router, self.logits, self.topk_idx,
+                              self.topk_gate, self.dgate, self.offsets, self.sorted_token,
+                              self.dz, self.dx_router, self.dw_router, stream)
+
+    def unpermute_sum(self, stream=None):
+        L.moe_unpermute_sum(self.p, self.dx_sorted, self.inv_perm, self.dx_router, self.dx,
+                            stream)
+
+    def backward(self, dy, stream=None):
+        """Gradients of sum(dy * y) for the last forward (train=True): returns self.dx and
+        fills dw_router, dw13, dw2 (fp32).  The routing bias has no gradient."""
+        assert self.train, "construct the layer with train=True"
+        self.combine_backward(dy, stream)
+        self.router_backward(stream)
+        self.expert_ffn_backward_input(stream)
+        self.expert_ffn_backward_weight(stream)
+        self.unpermute_sum(stream)
+        return self.dx
 
     def step(self, x, gamma=0.01, stream=None):
         y = self.forward(x, stream)

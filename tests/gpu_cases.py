@@ -6,6 +6,7 @@ import sys
 
 import numpy as np
 
+import oracle
 import workloads
 
 # name -> overrides of a base workload; small enough for the oracle to finish in
@@ -60,3 +61,43 @@ def shape_of(w):
     from mixture_experts_layer_added_amd.layer import Shape
     return Shape(T=w.T, H=w.H, E=w.E, G=w.G, M=w.M, K=w.K, J=w.J, I=w.I, S=w.S, act=w.act,
                  expert=w.expert)
+
+
+def token_reference(w, t, xn, wr, z, idx, gate, dyn, w13_of, w2_of):
+    """Oracle backward of token t alone (its K expert rows and its shared row): the
+    full problem restricted to one token.  w13_of(g), w2_of(g) give expert g's weights."""
+    bf = oracle.BF16 if w.act == "bf16" else oracle.F32
+    K = w.K
+    groups = [int(e) for e in idx[t]] + ([w.E] if w.S else [])
+    xt = np.ascontiguousarray(xn[t:t + 1])
+    w13 = {g: w13_of(g) for g in groups}
+    w2 = {g: w2_of(g) for g in groups}
+    ys = np.concatenate([oracle.expert_ffn(xt, w13[g], w2[g], bf, nthreads=1) for g in groups])
+    inv1 = np.arange(K, dtype=np.int32)[None, :]
+    dys, dg = oracle.combine_backward(dyn[t:t + 1], ys, inv1, gate[t:t + 1], w.S, nthreads=1)
+    dz, dxr, _ = oracle.router_backward(xt, wr, z[t:t + 1], idx[t:t + 1], gate[t:t + 1], dg,
+                                        nthreads=1)
+    dxs = np.empty((len(groups), w.H), xt.dtype)
+    dau = np.empty((len(groups), 2 * w.I), xt.dtype)
+    for i, g in enumerate(groups):
+        _, dau[i:i + 1], dxs[i:i + 1], _, _ = oracle.expert_backward(xt, w13[g], w2[g],
+                                                                     dys[i:i + 1], nthreads=1)
+    dx = oracle.unpermute_sum(dxs, inv1, dxr, 1, w.S, nthreads=1)
+    return dict(dgate=dg[0], dz=dz[0], dy_sorted=dys, dau=dau, dx=dx[0])
+
+
+def slice_reference(w, g, n, xn, tokens, gates, dyn, w13_of, w2_of):
+    """Oracle dW2[g][:, n], dW13[g][n, :], dW13[g][I+n, :] and [da|du][:, (n, I+n)] from
+    the rows of expert g (tokens, their gates) with the weights cut to column n."""
+    I = w.I
+    w13 = w13_of(g)
+    w13s = np.ascontiguousarray(w13[[n, I + n], :])
+    w2s = np.ascontiguousarray(w2_of(g)[:, n:n + 1])
+    m = len(tokens)
+    inv1 = np.arange(m, dtype=np.int32)[:, None]
+    dys, _ = oracle.combine_backward(np.ascontiguousarray(dyn[tokens]),
+                                     np.zeros((m, w.H), dyn.dtype), inv1,
+                                     np.ascontiguousarray(gates[:, None], np.float32), 0)
+    _, dau, _, dw13s, dw2s = oracle.expert_backward(np.ascontiguousarray(xn[tokens]), w13s, w2s,
+                                                    dys)
+    return dict(dw2=dw2s[:, 0], dw13_a=dw13s[0], dw13_u=dw13s[1], dau=dau)

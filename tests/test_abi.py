@@ -157,3 +157,43 @@ def test_gather_entry_points_validate(L):
     # permute without x_sorted needs no x
     rc = lib.moe_permute(ctypes.byref(p), None, None, d, d, d, None, None, d, 1 << 20, None)
     assert rc == L.MOE_ERR_INVALID_ARG and "topk_idx" in L.last_error()
+
+
+def test_backward_entry_points_validate(L):
+    lib = L.lib()
+    d = ctypes.c_void_p(4096)
+    p = prob(L, act_dtype=1, expert_dtype=1)
+    p8 = prob(L, act_dtype=1, expert_dtype=2)
+    bad = prob(L, act_dtype=1, expert_dtype=1, K=0)
+    calls = {
+        "moe_combine_backward": lambda q, n=d: lib.moe_combine_backward(
+            ctypes.byref(q), n, d, d, d, d, d, None),
+        "moe_router_backward": lambda q, n=d: lib.moe_router_backward(
+            ctypes.byref(q), n, d, d, d, d, d, d, d, d, d, d, None),
+        "moe_unpermute_sum": lambda q, n=d: lib.moe_unpermute_sum(
+            ctypes.byref(q), n, d, None, d, None),
+        "moe_expert_ffn_up_save": lambda q, n=d: lib.moe_expert_ffn_up_save(
+            ctypes.byref(q), n, None, d, d, d, d, None),
+        "moe_expert_ffn_backward_input": lambda q, n=d: lib.moe_expert_ffn_backward_input(
+            ctypes.byref(q), d, d, d, d, n, d, d, None),
+        "moe_expert_ffn_backward_weight": lambda q, n=d: lib.moe_expert_ffn_backward_weight(
+            ctypes.byref(q), n, None, d, d, d, d, d, d, None),
+    }
+    for name, call in calls.items():
+        # the FP8 expert path has no backward
+        assert call(p8) == L.MOE_ERR_UNSUPPORTED, name
+        assert name in L.last_error() and "bf16" in L.last_error()
+        assert call(bad) == L.MOE_ERR_INVALID_ARG and "K=" in L.last_error(), name
+        assert call(p, None) == L.MOE_ERR_INVALID_ARG, name
+        assert "NULL" in L.last_error(), name
+    # misaligned router gradient rows
+    rc = lib.moe_unpermute_sum(ctypes.byref(p), d, d, ctypes.c_void_p(4100), d, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "aligned" in L.last_error()
+    rc = lib.moe_combine_backward(ctypes.byref(p), d, d, None, d, d, d, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "inv_perm" in L.last_error()
+    # 32-bit row offsets of the backward GEMMs
+    big = prob(L, T=30000, H=7168, E=256, G=8, M=4, K=8, J=2, I=2048, act_dtype=1, expert_dtype=1)
+    rc = lib.moe_expert_ffn_backward_input(ctypes.byref(big), d, d, d, d, d, d, d, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "2^31" in L.last_error()
+    rc = lib.moe_expert_ffn_backward_weight(ctypes.byref(big), d, None, d, d, d, d, d, d, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "2^31" in L.last_error()

@@ -135,3 +135,40 @@ def test_bf16_backward_tracks_f32():
         a = oracle.bf16_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
         ref = bf[k].astype(np.float64)
         assert np.abs(a - ref).max() <= 2e-2 * np.abs(ref).max(), k
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_local_decompositions_match_full_backward(act):
+    """The full-size GPU test checks the backward through one-token problems and
+    column-sliced expert problems; both must equal the full oracle backward exactly
+    (same arithmetic on the same values), here on a small layer."""
+    from gpu_cases import slice_reference, token_reference
+    from types import SimpleNamespace
+    x, wr, bias, w13, w2, dy = make(seed=4, T=20, H=128, E=8, I=16)
+    if act == "bf16":
+        cv = lambda a: oracle.bf16_from_f64_array(a.astype(np.float64))  # noqa: E731
+        x, w13, w2, dy = cv(x), cv(w13), cv(w2), cv(dy)
+    fwd, bw = oracle_grads(x, wr, bias, w13, w2, dy)
+    _, _, _, z = oracle.route(x, wr, bias, G, M, K, J, want_logits=True)
+    E, I, T = wr.shape[0], w2.shape[2], x.shape[0]
+    w = SimpleNamespace(T=T, H=x.shape[1], E=E, K=K, I=I, S=1, act=act)
+    idx, gate, inv = fwd["topk_idx"], fwd["topk_gate"], fwd["inv_perm"]
+    for t in (0, 7, T - 1):
+        r = token_reference(w, t, x, wr, z, idx, gate, dy, lambda g: w13[g], lambda g: w2[g])
+        assert np.array_equal(r["dgate"].view(np.uint32), bw["dgate"][t].view(np.uint32))
+        assert np.array_equal(r["dz"].view(np.uint32), bw["dz"][t].view(np.uint32))
+        rows = list(inv[t]) + [T * K + t]
+        assert np.array_equal(r["dy_sorted"], bw["dy_sorted"][rows])
+        assert np.array_equal(r["dau"], bw["dau"][rows])
+        assert np.array_equal(r["dx"], bw["dx"][t])
+    off, st = fwd["offsets"], fwd["sorted_token"]
+    for g in (int(np.argmax(fwd["counts"])), E):
+        toks = st[off[g]:off[g + 1]].astype(np.int64)
+        gates = (gate[toks, np.argmax(idx[toks] == g, axis=1)] if g < E
+                 else np.ones(len(toks), np.float32))
+        for n in (0, 5, I - 1):
+            r = slice_reference(w, g, n, x, toks, gates, dy, lambda e: w13[e], lambda e: w2[e])
+            assert np.array_equal(r["dw2"], bw["dw2"][g][:, n])
+            assert np.array_equal(r["dw13_a"], bw["dw13"][g][n])
+            assert np.array_equal(r["dw13_u"], bw["dw13"][g][I + n])
+            assert np.array_equal(r["dau"], bw["dau"][off[g]:off[g + 1]][:, [n, I + n]])

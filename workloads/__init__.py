@@ -180,6 +180,13 @@ def make_x(w: Workload, step: int = 0, device="cpu", T: int | None = None):
     return x
 
 
+def make_dy(w: Workload, device="cpu"):
+    """Output gradient [T,H] ~ N(0,1) in the activation dtype (its own seeded stream),
+    for the backward."""
+    g = _gen(w.seed_x + 1_000_003, device)
+    return _normal((w.T, w.H), 1.0, act_dtype(w), g, device)
+
+
 def make_y_sorted(w: Workload, seed: int, device="cpu"):
     """Random expert outputs [R,H] for testing the combine step on its own."""
     torch = _torch()

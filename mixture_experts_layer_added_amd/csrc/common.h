@@ -49,6 +49,14 @@ __device__ __forceinline__ void load4_to_lds(i32x4 rsrc, uint32_t lds, uint32_t 
 
 // Wait until at most n (0..15) vector-memory operations of this wave are outstanding;
 // other n wait for all.
+// s_waitcnt vmcnt(N) for a compile-time N in [0, 63] (6-bit counter: bits 3:0 and
+// 15:14 of the immediate); expcnt and lgkmcnt left unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 __device__ __forceinline__ void wait_vmcnt(int n) {
   switch (n) {
 #define MOE_VMCNT_CASE(k) \

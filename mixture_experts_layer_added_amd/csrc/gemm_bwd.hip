@@ -46,17 +46,26 @@ __device__ __forceinline__ int swz_a(int r, int c) { return r * kARow + ((c ^ (r
 // in 8 distinct bank groups.
 __device__ __forceinline__ int swz_o(int r, int c) { return r * kORow + ((c ^ (2 * (r & 3))) << 4); }
 
-// 8 consecutive k (16*s .. +7 within the stage, from 8 * (lane / 32)) of column
-// nb + lane % 32 of a K-outer stage at LDS offset `st`.
-__device__ __forceinline__ bf16x8 frag_kouter(const char* st, int nb, int s, int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const int n = nb + 16 * (g & 1) + 4 * (j & 3);
-  const int k0 = 16 * s + 8 * (g >> 1) + (j >> 2);
-  const int off_n = (n & 7) * 2;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(uintptr_t)(lds_offset(st) + swz_o(k0, n >> 3) + off_n));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(uintptr_t)(lds_offset(st) + swz_o(k0 + 4, n >> 3) + off_n));
+// Lane part of the LDS byte offset of a K-outer fragment read, for fragment columns
+// nb with (nb / 32) & 1 == par.  In each 16-lane group g, source lane j reads k-row
+// 8 (g >> 1) + j / 4 and 4 columns starting at 16 (g & 1) + 4 (j & 3); the chunk swizzle
+// stays inside an aligned group of 8 chunks (64 columns), so the fragment at columns
+// nb, k-step s (16 k-rows), upper half (k + 4) sits at
+//   kouter_lane_off(lane, par) + (nb / 64) * 128 + s * 8192 + hi * 2048,
+// constants the compiler folds into the read's offset field.
+__device__ __forceinline__ uint32_t kouter_lane_off(int lane, int par) {
+  const int g = lane >> 4, j = lane & 15, i = j >> 2;
+  const int row = 8 * (g >> 1) + i;
+  const int c = 4 * par + 2 * (g & 1) + ((j & 3) >> 1);
+  return (uint32_t)(row * kORow + ((c ^ (2 * i)) << 4) + (j & 1) * 8);
+}
+
+// 8 consecutive k of one column per lane (the v_mfma_f32_32x32x16_bf16 operand layout)
+// from a K-outer stage: `addr` is the LDS byte address of the lower read.
+__device__ __forceinline__ bf16x8 frag_ko(uint32_t addr) {
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)addr);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(addr + 4 * kORow));
   bf16x8 f;
   const v4i16 both[2] = {lo, hi};
   __builtin_memcpy(&f, both, 16);
@@ -100,6 +109,29 @@ __device__ __forceinline__ void kouter_issue(const KOuterLoader& L, uint32_t lds
       const int grow = gather ? gather[rowbase + kr] : rowbase + kr;
       voff = (uint32_t)grow * (uint32_t)ld * 2u + L.off[j];
     }
+    load16_to_lds(L.rsrc, lds_stage + (4 * wv + j) * 1024, voff);
+  }
+}
+
+// The same stage in two halves: the matrix row of each of this lane's 4 loads (-1:
+// outside, read as zeros), then the loads.  Fetching the gather indices ahead lets the
+// loads themselves be issued without waiting on index reads.
+__device__ __forceinline__ void kouter_rows(const KOuterLoader& L, int k0, int krows, int rowbase,
+                                            const int32_t* __restrict__ gather, int rows[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int kr = k0 + L.krow[j];
+    rows[j] = -1;
+    if (kr < krows && L.row_ok[j]) rows[j] = gather ? gather[rowbase + kr] : rowbase + kr;
+  }
+}
+
+__device__ __forceinline__ void kouter_issue_rows(const KOuterLoader& L, uint32_t lds_stage,
+                                                  int wv, int ld, const int rows[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t voff =
+        rows[j] >= 0 ? (uint32_t)rows[j] * (uint32_t)ld * 2u + L.off[j] : 0x7ffffff0u;
     load16_to_lds(L.rsrc, lds_stage + (4 * wv + j) * 1024, voff);
   }
 }
@@ -161,6 +193,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nn_bf16(
     KOuterLoader bl;
     kouter_setup(bl, B + (int64_t)tl.g * Kd * N, Kd, N, n0, N, lane, wv);
     const uint32_t ldsw = lds0 + 8 * wv * kARow;
+    const uint32_t lo_b[2] = {lds0 + kouter_lane_off(lane, 0), lds0 + kouter_lane_off(lane, 1)};
 
 #define NN_STAGE_LOAD(kt, st)                                                         \
   {                                                                                   \
@@ -196,13 +229,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nn_bf16(
       }
       if (w_on) {
         const char* as = smem + st * sStage;
-        const char* bs = as + sA;
+        const uint32_t boff = st * sStage + sA + 2 * wn * 128;
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
           const int c = 2 * s + kq;
           bf16x8 b[4];
 #pragma unroll
-          for (int n = 0; n < 4; ++n) b[n] = frag_kouter(bs, 128 * wn + 32 * n, s, lane);
+          for (int n = 0; n < 4; ++n)
+            b[n] = frag_ko(lo_b[n & 1] + boff + (n >> 1) * 128 + s * 16 * kORow);
           const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(as + swz_a(arow0, c));
 #pragma unroll
           for (int n = 0; n < 4; ++n)
@@ -252,7 +286,107 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nn_bf16(
 //   A: [R, M] rows; B: [R, N] rows (or, with gather, [T, N] rows gather[r]).
 // Tiles (group, i-tile, n-tile), 256 x 256, k steps of 64 rows; both operands K-outer
 // (two 32 KiB stages of each, double-buffered).  Groups without rows write zeros.
+//
+// With ~128 rows per expert a tile is 2 k-steps of MFMA work and 256 KiB of fp32
+// output, so the kernel is bound by HBM writes.  Two choices keep the write stream
+// going:
+//  * the MFMA takes the B fragment as its first operand, so a lane's accumulator holds
+//    4 consecutive n of one output row: each lane writes 16 bytes per store, 32 stores
+//    per tile, every one issued (lanes outside the matrix point past the end of the
+//    buffer and are dropped), so the count is exact;
+//  * the first two k-stages of the NEXT tile are issued before this tile's stores.
+//    Vector memory operations complete in issue order, so the wait for those stages
+//    leaves this tile's 32 stores outstanding (vmcnt <= 32 (+8 for the second stage))
+//    and the stores drain while the next tile computes.
 // ---------------------------------------------------------------------------
+constexpr int kTnStores = 32;  // 16-byte stores per lane per tile
+
+// K-outer stage loader of the wgrad kernel: the column (within the matrix) of this
+// lane's 16 bytes for each of its 4 load instructions; k-rows as in kouter_setup.
+struct TnLoader {
+  i32x4 rsrc;
+  int col[4];
+};
+
+__device__ __forceinline__ int tn_krow(int wv, int j, int lane) {
+  return 2 * (4 * wv + j) + (lane >> 5);
+}
+
+__device__ __forceinline__ void tn_setup(TnLoader& L, const void* base, int64_t nrows, int ld,
+                                         int col0, int lane) {
+  L.rsrc = buffer_rsrc(base, (uint32_t)(nrows * ld * 2));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 2 * j + (lane >> 5);  // k-row mod 4 (the 8 wv term drops out)
+    L.col[j] = col0 + 8 * ((lane & 31) ^ (2 * (r & 3)));
+  }
+}
+
+// matrix rows of stage k0 for this lane's 4 loads (-1: outside, read as zeros)
+__device__ __forceinline__ void tn_rows(int wv, int lane, int k0, int m_g, int row0,
+                                        const int32_t* __restrict__ gather, int rows[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int kr = k0 + tn_krow(wv, j, lane);
+    rows[j] = -1;
+    if (kr < m_g) rows[j] = gather ? gather[row0 + kr] : row0 + kr;
+  }
+}
+
+__device__ __forceinline__ void tn_issue(const TnLoader& L, uint32_t lds_stage, int wv, int ld,
+                                         const int rows[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t voff = (rows[j] >= 0 && L.col[j] < ld)
+                              ? ((uint32_t)rows[j] * (uint32_t)ld + (uint32_t)L.col[j]) * 2u
+                              : 0x7ffffff0u;
+    load16_to_lds(L.rsrc, lds_stage + (4 * wv + j) * 1024, voff);
+  }
+}
+
+struct TnTile {
+  int g, i0, n0, row0, m_g, nk;
+};
+
+__device__ __forceinline__ TnTile tn_tile(int tile, int mtn, int ntn,
+                                          const int32_t* __restrict__ offsets) {
+  TnTile t;
+  t.g = __builtin_amdgcn_readfirstlane(tile / (mtn * ntn));
+  const int rem = tile - t.g * mtn * ntn;
+  t.i0 = __builtin_amdgcn_readfirstlane(rem / ntn) * BM;
+  t.n0 = __builtin_amdgcn_readfirstlane(rem % ntn) * BN;
+  t.row0 = __builtin_amdgcn_readfirstlane(offsets[t.g]);
+  t.m_g = __builtin_amdgcn_readfirstlane(offsets[t.g + 1]) - t.row0;
+  t.nk = (t.m_g + BK - 1) / BK;
+  return t;
+}
+
+// Stages 0 and 1 of tile t into the two LDS buffers; every index read (stages 0-2) is
+// made before the first load is issued, so issuing never waits on memory.
+__device__ __forceinline__ void tn_prefetch(const TnTile& t, const TnLoader& al,
+                                            const TnLoader& bl, int wv, int lane, uint32_t lds0,
+                                            int M, int N, const int32_t* __restrict__ gather,
+                                            int rB2[4]) {
+  int ra0[4], ra1[4], rb0[4], rb1[4];
+  tn_rows(wv, lane, 0, t.m_g, t.row0, gather, rb0);
+  tn_rows(wv, lane, BK, t.m_g, t.row0, gather, rb1);
+  tn_rows(wv, lane, 2 * BK, t.m_g, t.row0, gather, rB2);
+  tn_rows(wv, lane, 0, t.m_g, t.row0, nullptr, ra0);
+  tn_rows(wv, lane, BK, t.m_g, t.row0, nullptr, ra1);
+  // the index reads are the youngest memory operations here: wait for them before
+  // the loads, so no wait for an index lands between loads (it would also wait for
+  // the loads issued before it)
+  wait_vm<0>();
+  if (t.nk > 0) {
+    tn_issue(al, lds0, wv, M, ra0);
+    tn_issue(bl, lds0 + kOStage, wv, N, rb0);
+  }
+  if (t.nk > 1) {
+    tn_issue(al, lds0 + 2 * kOStage, wv, M, ra1);
+    tn_issue(bl, lds0 + 3 * kOStage, wv, N, rb1);
+  }
+}
+
 __global__ __launch_bounds__(512, 1) void k_gemm_tn_bf16(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const int32_t* __restrict__ gather, int64_t b_rows, float* __restrict__ Cw,
@@ -265,30 +399,37 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tn_bf16(
   const int mtn = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
   const int ntiles = NG * mtn * ntn;
   const int64_t R = offsets[NG];
+  const int64_t brows = gather ? b_rows : R;
+  const uint32_t out_bytes = (uint32_t)M * (uint32_t)N * 4u;  // <= 2^31 (checked on the host)
 
   const int P = gridDim.x, per_xcd = P / kXcds;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int chunk = (ntiles + kXcds - 1) / kXcds;
   const int end = min(ntiles, (xcd + 1) * chunk);
-  for (int tile = xcd * chunk + slot; tile < end; tile += per_xcd) {
-    const int g = __builtin_amdgcn_readfirstlane(tile / (mtn * ntn));
-    const int rem = tile - g * mtn * ntn;
-    const int i0 = __builtin_amdgcn_readfirstlane(rem / ntn) * BM;
-    const int n0 = __builtin_amdgcn_readfirstlane(rem % ntn) * BN;
-    const int row0 = offsets[g];
-    const int m_g = offsets[g + 1] - row0;
-    const int nk = (m_g + BK - 1) / BK;
+  int tile = xcd * chunk + slot;
+  if (tile >= end) return;
 
-    KOuterLoader al, bl;
-    kouter_setup(al, A, R, M, i0, M, lane, wv);
-    kouter_setup(bl, B, gather ? b_rows : R, N, n0, N, lane, wv);
+  // Vector memory operations complete in issue order.  Every tile's first two k-stages
+  // are issued before the previous tile's 32 stores, so waiting until at most 32
+  // operations are outstanding leaves those stores draining while the tile computes.
+  // The first tile follows 32 stores that point past the end of the output (dropped),
+  // so the count is the same for every tile.
+  const __amdgpu_buffer_rsrc_t out0 =
+      __builtin_amdgcn_make_buffer_rsrc(Cw, (short)0, (int)out_bytes, 0x00020000);
+  const uint32_t lo_f[2] = {lds0 + kouter_lane_off(lane, 0), lds0 + kouter_lane_off(lane, 1)};
+  const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
-#define TN_STAGE_LOAD(kt, st)                                                                  \
-  {                                                                                            \
-    kouter_issue(al, lds0 + (st) * 2 * kOStage, wv, (kt) * BK, m_g, M, row0, nullptr);         \
-    kouter_issue(bl, lds0 + (st) * 2 * kOStage + kOStage, wv, (kt) * BK, m_g, N, row0, gather); \
-  }
+  TnTile t = tn_tile(tile, mtn, ntn, offsets);
+  TnLoader al, bl;
+  tn_setup(al, A, R, M, t.i0, lane);
+  tn_setup(bl, B, brows, N, t.n0, lane);
+  int rB2[4];  // B rows of stage 2 (gather indices fetched ahead)
+  tn_prefetch(t, al, bl, wv, lane, lds0, M, N, gather, rB2);
+#pragma unroll
+  for (int q = 0; q < kTnStores; ++q)  // distinct addresses, so none is merged away
+    __builtin_amdgcn_raw_buffer_store_b128(zero4, out0, out_bytes + 16u * q, 0, 0);
 
+  for (;;) {
     f32x16 acc[2][4];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
@@ -297,43 +438,75 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tn_bf16(
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[mi][n][i] = 0.0f;
 
-    __syncthreads();
-    if (nk > 0) TN_STAGE_LOAD(0, 0)
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_vmcnt(0);
+    for (int kt = 0; kt < t.nk; ++kt) {
+      if (kt < 2) wait_vm<kTnStores>();
+      else wait_vm<0>();
       __syncthreads();
-      if (kt + 1 < nk) TN_STAGE_LOAD(kt + 1, (kt + 1) & 1)
-      const char* as = smem + (kt & 1) * 2 * kOStage;
-      const char* bs = as + kOStage;
+      if (kt >= 1 && kt + 1 < t.nk) {  // stage kt+1 >= 2 into the buffer stage kt-1 used
+        const uint32_t sb = lds0 + ((kt + 1) & 1) * 2 * kOStage;
+        int ra[4], rb[4];
+        tn_rows(wv, lane, (kt + 1) * BK, t.m_g, t.row0, nullptr, ra);
+        if (kt == 1) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) rb[j] = rB2[j];
+        } else {
+          tn_rows(wv, lane, (kt + 1) * BK, t.m_g, t.row0, gather, rb);
+          wait_vm<0>();  // only these index reads are outstanding here
+        }
+        tn_issue(al, sb, wv, M, ra);
+        tn_issue(bl, sb + kOStage, wv, N, rb);
+      }
+      const uint32_t aoff = (kt & 1) * 2 * kOStage + wm * 128;
+      const uint32_t boff = (kt & 1) * 2 * kOStage + kOStage + 2 * wn * 128;
 #pragma unroll
       for (int s = 0; s < BK / 16; ++s) {
         bf16x8 b[4];
 #pragma unroll
-        for (int n = 0; n < 4; ++n) b[n] = frag_kouter(bs, 128 * wn + 32 * n, s, lane);
+        for (int n = 0; n < 4; ++n)
+          b[n] = frag_ko(lo_f[n & 1] + boff + (n >> 1) * 128 + s * 16 * kORow);
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
-          const bf16x8 a = frag_kouter(as, 64 * wm + 32 * mi, s, lane);
+          const bf16x8 a = frag_ko(lo_f[mi] + aoff + s * 16 * kORow);
 #pragma unroll
-          for (int n = 0; n < 4; ++n)
-            acc[mi][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[n], acc[mi][n], 0, 0, 0);
+          for (int n = 0; n < 4; ++n)  // output row = A column, 4 consecutive n per lane
+            acc[mi][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[n], a, acc[mi][n], 0, 0, 0);
         }
       }
     }
-#undef TN_STAGE_LOAD
 
-    float* cw = Cw + (int64_t)g * M * N;
+    // the next tile: its rows, then (LDS free) its first two stages
+    const int next = tile + per_xcd;
+    const bool has_next = next < end;
+    const TnTile cur = t;
+    __syncthreads();  // every wave is done with this tile's LDS
+    if (has_next) {
+      t = tn_tile(next, mtn, ntn, offsets);
+      tn_setup(al, A, R, M, t.i0, lane);
+      tn_setup(bl, B, brows, N, t.n0, lane);
+      tn_prefetch(t, al, bl, wv, lane, lds0, M, N, gather, rB2);
+    }
+
+    // this tile's stores: lane holds output row i (its MFMA column) and 4 consecutive n
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        Cw + (int64_t)cur.g * M * N, (short)0, (int)out_bytes, 0x00020000);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < 2; ++mi) {
+      const int row = cur.i0 + 64 * wm + 32 * mi + (lane & 31);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = i0 + 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (row >= M) continue;
+      for (int n = 0; n < 4; ++n)
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const int col = n0 + 128 * wn + 32 * n + (lane & 31);
-          if (col < N) cw[(int64_t)row * N + col] = acc[mi][n][i];
+        for (int j = 0; j < 4; ++j) {
+          const int col = cur.n0 + 128 * wn + 32 * n + 8 * j + 4 * (lane >> 5);
+          const uint32_t off = (row < M && col < N)
+                                   ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 4u
+                                   : out_bytes;  // past the end: dropped
+          const f32x4 v = {acc[mi][n][4 * j], acc[mi][n][4 * j + 1], acc[mi][n][4 * j + 2],
+                           acc[mi][n][4 * j + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(v, crs, off, 0, 0);
         }
-      }
+    }
+    if (!has_next) break;
+    tile = next;
   }
 }
 

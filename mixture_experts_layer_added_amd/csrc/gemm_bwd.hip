@@ -284,229 +284,287 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nn_bf16(
 // ---------------------------------------------------------------------------
 // wgrad:  Cw[g][i, n] = sum over the rows r of group g of A[r, i] B[r, n]  (fp32 out)
 //   A: [R, M] rows; B: [R, N] rows (or, with gather, [T, N] rows gather[r]).
-// Tiles (group, i-tile, n-tile), 256 x 256, k steps of 64 rows; both operands K-outer
-// (two 32 KiB stages of each, double-buffered).  Groups without rows write zeros.
+// Tiles (group, i-tile, n-tile) of 256 x 256; both operands K-outer.  Groups without
+// rows write zeros.
 //
-// With ~128 rows per expert a tile is 2 k-steps of MFMA work and 256 KiB of fp32
-// output, so the kernel is bound by HBM writes.  Two choices keep the write stream
-// going:
-//  * the MFMA takes the B fragment as its first operand, so a lane's accumulator holds
-//    4 consecutive n of one output row: each lane writes 16 bytes per store, 32 stores
-//    per tile, every one issued (lanes outside the matrix point past the end of the
-//    buffer and are dropped), so the count is exact;
-//  * the first two k-stages of the NEXT tile are issued before this tile's stores.
-//    Vector memory operations complete in issue order, so the wait for those stages
-//    leaves this tile's 32 stores outstanding (vmcnt <= 32 (+8 for the second stage))
-//    and the stores drain while the next tile computes.
+// With ~128 rows per expert a tile is little MFMA work and 256 KiB of fp32 output, so
+// the kernel is bound by HBM writes, and the loads must not wait behind the stores.
+//  * The k-stages (32 rows of both operands, 32 KiB) of all the workgroup's tiles form
+//    one stream: stage q is loaded kTAhead steps before it is computed, into LDS buffer
+//    q % kTRing, across tile boundaries.  With gather, the 32 row indices of stage q
+//    are themselves loaded into LDS kTAhead steps before the stage.
+//  * Vector memory operations complete in issue order, and every step issues the same
+//    number of loads (dummy ones past the end of the stream), so the wait for stage q
+//    is "at most (kTAhead-1) steps of loads plus the stores issued since are
+//    outstanding"; stores of a finished tile drain while later stages load.
+//  * The MFMA takes the row operand second, so a lane holds 4 consecutive outputs of
+//    one row; the tile goes out through the LDS buffer of its last stage as 32 stores
+//    of 16 bytes per lane that each cover 8 whole 128-byte rows (partial-line writes
+//    make the L2 fetch the rest of the line first), every one issued (lanes outside
+//    the matrix write past the end of the buffer, which drops them).
 // ---------------------------------------------------------------------------
-constexpr int kTnStores = 32;  // 16-byte stores per lane per tile
+constexpr int kTK = 32;                // rows of each operand per stage
+constexpr int kTOp = kTK * kORow;      // 16 KiB: one operand of one stage
+constexpr int kTRing = 4;              // stages held in LDS
+constexpr int kTAhead = 3;             // stages in flight ahead of the one computed
+constexpr int kTIdx = 8;               // gather-index slots of 64 ints (> kTAhead)
+constexpr int kTStores = 32;           // 16-byte stores per lane per tile
+static_assert(kTAhead < kTRing, "the buffer refilled at a step was computed the step before");
 
-// K-outer stage loader of the wgrad kernel: the column (within the matrix) of this
-// lane's 16 bytes for each of its 4 load instructions; k-rows as in kouter_setup.
-struct TnLoader {
-  i32x4 rsrc;
-  int col[4];
+struct TnCursor {
+  int q;                         // position in the stage stream
+  int tile;                      // >= end: past the end of the stream
+  int kt, nk, g, i0, n0, row0, m_g;
 };
 
-__device__ __forceinline__ int tn_krow(int wv, int j, int lane) {
-  return 2 * (4 * wv + j) + (lane >> 5);
+__device__ __forceinline__ void tn_tile_params(TnCursor& c, int tile, int mtn, int ntn,
+                                               const int* s_off) {
+  c.tile = tile;
+  c.kt = 0;
+  c.g = __builtin_amdgcn_readfirstlane(tile / (mtn * ntn));
+  const int rem = tile - c.g * mtn * ntn;
+  c.i0 = __builtin_amdgcn_readfirstlane(rem / ntn) * BM;
+  c.n0 = __builtin_amdgcn_readfirstlane(rem % ntn) * BN;
+  c.row0 = __builtin_amdgcn_readfirstlane(s_off[c.g]);
+  c.m_g = __builtin_amdgcn_readfirstlane(s_off[c.g + 1]) - c.row0;
+  c.nk = (c.m_g + kTK - 1) / kTK;
 }
 
-__device__ __forceinline__ void tn_setup(TnLoader& L, const void* base, int64_t nrows, int ld,
-                                         int col0, int lane) {
-  L.rsrc = buffer_rsrc(base, (uint32_t)(nrows * ld * 2));
+// first stage at or after tile `from` (tiles without rows are skipped)
+__device__ __forceinline__ void tn_seek(TnCursor& c, int from, int end, int step, int mtn,
+                                        int ntn, const int* s_off) {
+  for (int t = from; t < end; t += step) {
+    tn_tile_params(c, t, mtn, ntn, s_off);
+    if (c.nk > 0) return;
+  }
+  c.tile = end;
+}
+
+__device__ __forceinline__ void tn_advance(TnCursor& c, int end, int step, int mtn, int ntn,
+                                           const int* s_off) {
+  ++c.q;
+  if (c.tile >= end) return;
+  if (++c.kt < c.nk) return;
+  tn_seek(c, c.tile + step, end, step, mtn, ntn, s_off);
+}
+
+// LDS column offset (bytes within a 512-byte k-row) and matrix column of this lane's
+// 16 bytes for load instruction j; k-row of instruction j is 2 (2 wv + j) + lane / 32.
+__device__ __forceinline__ int tn_chunk(int j, int lane) {
+  const int r = 2 * j + (lane >> 5);  // k-row mod 4
+  return (lane & 31) ^ (2 * (r & 3));
+}
+
+// the 32 gather indices of stage x into its 256-byte slot (lanes 32-63 fill the upper
+// half of the slot with zeros)
+template <bool kGather>
+__device__ __forceinline__ void tn_issue_index(const TnCursor& x, bool live, i32x4 grs,
+                                               uint32_t lds_idx, int lane) {
+  if (!kGather) return;
+  uint32_t voff = 0x7ffffff0u;
+  const int kr = x.kt * kTK + lane;
+  if (live && lane < kTK && kr < x.m_g) voff = (uint32_t)(x.row0 + kr) * 4u;
+  load4_to_lds(grs, __builtin_amdgcn_readfirstlane(lds_idx + (x.q % kTIdx) * 256), voff);
+}
+
+template <bool kGather>
+__device__ __forceinline__ void tn_issue_stage(const TnCursor& d, bool live, i32x4 ars, i32x4 brs,
+                                               uint32_t lds0, const int* s_idx, int wv, int lane,
+                                               int M, int N) {
+  const uint32_t buf = __builtin_amdgcn_readfirstlane(lds0 + (d.q % kTRing) * 2 * kTOp);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 2 * j + (lane >> 5);  // k-row mod 4 (the 8 wv term drops out)
-    L.col[j] = col0 + 8 * ((lane & 31) ^ (2 * (r & 3)));
+  for (int j = 0; j < 2; ++j) {
+    const int kr = d.kt * kTK + 2 * (2 * wv + j) + (lane >> 5);
+    const bool row_ok = live && kr < d.m_g;
+    const int c8 = 8 * tn_chunk(j, lane);
+    uint32_t va = 0x7ffffff0u, vb = 0x7ffffff0u;
+    if (row_ok && d.i0 + c8 < M) va = ((uint32_t)(d.row0 + kr) * (uint32_t)M + d.i0 + c8) * 2u;
+    if (row_ok && d.n0 + c8 < N) {
+      const int brow = kGather ? s_idx[(d.q % kTIdx) * 64 + kr - d.kt * kTK] : d.row0 + kr;
+      vb = ((uint32_t)brow * (uint32_t)N + d.n0 + c8) * 2u;
+    }
+    load16_to_lds(ars, buf + (2 * wv + j) * 1024, va);
+    load16_to_lds(brs, buf + kTOp + (2 * wv + j) * 1024, vb);
   }
 }
 
-// matrix rows of stage k0 for this lane's 4 loads (-1: outside, read as zeros)
-__device__ __forceinline__ void tn_rows(int wv, int lane, int k0, int m_g, int row0,
-                                        const int32_t* __restrict__ gather, int rows[4]) {
+template <bool kGather>
+__device__ __forceinline__ void tn_wait(int b) {
+  constexpr int base = (kTAhead - 1) * (4 + (kGather ? 1 : 0));
+  if (b == 0) wait_vm<base>();
+  else wait_vm<base + kTStores>();  // two or more batches: waits for more than it needs
+}
+
+// Output of one tile.  Each wave's 64 x 128 block goes out as 8 sub-blocks of 32 x 32:
+// the accumulators (lane = output row, 4 consecutive columns) are written to the wave's
+// 4 KiB of `stage` (a free LDS buffer) and read back as 8 rows x 8 chunks of 16 bytes,
+// so every store writes 8 whole 128-byte rows.  Chunk c of row r sits at slot
+// c ^ (r & 7).  32 stores per lane; lanes outside the matrix write past its end
+// (dropped).  zero: store zeros without staging (tiles of groups without rows).
+__device__ __forceinline__ void tn_store(float* __restrict__ Cw, const f32x16 (&acc)[2][4],
+                                         int g, int i0, int n0, int M, int N, int wm, int wn,
+                                         int lane, char* stage, int wv, bool zero) {
+  const uint32_t out_bytes = (uint32_t)M * (uint32_t)N * 4u;
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      Cw + (int64_t)g * M * N, (short)0, (int)out_bytes, 0x00020000);
+  char* mine = stage + wv * 4096;
+  const int wr = lane & 31;                  // row this lane writes
+  const int rr = lane >> 3, rc = lane & 7;   // row (within 8) and chunk this lane reads
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int kr = k0 + tn_krow(wv, j, lane);
-    rows[j] = -1;
-    if (kr < m_g) rows[j] = gather ? gather[row0 + kr] : row0 + kr;
-  }
-}
-
-__device__ __forceinline__ void tn_issue(const TnLoader& L, uint32_t lds_stage, int wv, int ld,
-                                         const int rows[4]) {
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t voff = (rows[j] >= 0 && L.col[j] < ld)
-                              ? ((uint32_t)rows[j] * (uint32_t)ld + (uint32_t)L.col[j]) * 2u
-                              : 0x7ffffff0u;
-    load16_to_lds(L.rsrc, lds_stage + (4 * wv + j) * 1024, voff);
-  }
+    for (int n = 0; n < 4; ++n) {
+      if (!zero) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = 2 * j + (lane >> 5);
+          const f32x4 v = {acc[mi][n][4 * j], acc[mi][n][4 * j + 1], acc[mi][n][4 * j + 2],
+                           acc[mi][n][4 * j + 3]};
+          *reinterpret_cast<f32x4*>(mine + wr * 128 + ((c ^ (wr & 7)) << 4)) = v;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 8 * q + rr;
+        f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (!zero) v = *reinterpret_cast<const f32x4*>(mine + r * 128 + ((rc ^ (r & 7)) << 4));
+        const int row = i0 + 64 * wm + 32 * mi + r;
+        const int col = n0 + 128 * wn + 32 * n + 4 * rc;
+        const uint32_t off = (row < M && col < N)
+                                 ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 4u
+                                 : out_bytes;  // past the end: dropped
+        __builtin_amdgcn_raw_buffer_store_b128(v, crs, off, 0, 0);
+      }
+    }
 }
 
-struct TnTile {
-  int g, i0, n0, row0, m_g, nk;
-};
-
-__device__ __forceinline__ TnTile tn_tile(int tile, int mtn, int ntn,
-                                          const int32_t* __restrict__ offsets) {
-  TnTile t;
-  t.g = __builtin_amdgcn_readfirstlane(tile / (mtn * ntn));
-  const int rem = tile - t.g * mtn * ntn;
-  t.i0 = __builtin_amdgcn_readfirstlane(rem / ntn) * BM;
-  t.n0 = __builtin_amdgcn_readfirstlane(rem % ntn) * BN;
-  t.row0 = __builtin_amdgcn_readfirstlane(offsets[t.g]);
-  t.m_g = __builtin_amdgcn_readfirstlane(offsets[t.g + 1]) - t.row0;
-  t.nk = (t.m_g + BK - 1) / BK;
-  return t;
-}
-
-// Stages 0 and 1 of tile t into the two LDS buffers; every index read (stages 0-2) is
-// made before the first load is issued, so issuing never waits on memory.
-__device__ __forceinline__ void tn_prefetch(const TnTile& t, const TnLoader& al,
-                                            const TnLoader& bl, int wv, int lane, uint32_t lds0,
-                                            int M, int N, const int32_t* __restrict__ gather,
-                                            int rB2[4]) {
-  int ra0[4], ra1[4], rb0[4], rb1[4];
-  tn_rows(wv, lane, 0, t.m_g, t.row0, gather, rb0);
-  tn_rows(wv, lane, BK, t.m_g, t.row0, gather, rb1);
-  tn_rows(wv, lane, 2 * BK, t.m_g, t.row0, gather, rB2);
-  tn_rows(wv, lane, 0, t.m_g, t.row0, nullptr, ra0);
-  tn_rows(wv, lane, BK, t.m_g, t.row0, nullptr, ra1);
-  // the index reads are the youngest memory operations here: wait for them before
-  // the loads, so no wait for an index lands between loads (it would also wait for
-  // the loads issued before it)
-  wait_vm<0>();
-  if (t.nk > 0) {
-    tn_issue(al, lds0, wv, M, ra0);
-    tn_issue(bl, lds0 + kOStage, wv, N, rb0);
-  }
-  if (t.nk > 1) {
-    tn_issue(al, lds0 + 2 * kOStage, wv, M, ra1);
-    tn_issue(bl, lds0 + 3 * kOStage, wv, N, rb1);
-  }
-}
-
+template <bool kGather>
 __global__ __launch_bounds__(512, 1) void k_gemm_tn_bf16(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     const int32_t* __restrict__ gather, int64_t b_rows, float* __restrict__ Cw,
     const int32_t* __restrict__ offsets, int NG, int M, int N) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * kOStage];  // 128 KiB
+  __shared__ __attribute__((aligned(1024))) char smem[kTRing * 2 * kTOp];  // 128 KiB
+  __shared__ __attribute__((aligned(256))) int s_idx[kTIdx * 64];
+  __shared__ int s_off[kMaxGroups + 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 1, wn = wv & 1;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
+  const uint32_t lds_idx = __builtin_amdgcn_readfirstlane(lds_offset(s_idx));
+  for (int i = tid; i <= NG; i += 512) s_off[i] = offsets[i];
+  __syncthreads();
   const int mtn = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
   const int ntiles = NG * mtn * ntn;
-  const int64_t R = offsets[NG];
-  const int64_t brows = gather ? b_rows : R;
-  const uint32_t out_bytes = (uint32_t)M * (uint32_t)N * 4u;  // <= 2^31 (checked on the host)
+  const int64_t R = __builtin_amdgcn_readfirstlane(s_off[NG]);
+  const i32x4 ars = buffer_rsrc(A, (uint32_t)(R * M * 2));
+  const i32x4 brs = buffer_rsrc(B, (uint32_t)((kGather ? b_rows : R) * N * 2));
+  const i32x4 grs = buffer_rsrc(gather, (uint32_t)(R * 4));
 
-  const int P = gridDim.x, per_xcd = P / kXcds;
+  const int P = gridDim.x, step = P / kXcds;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int chunk = (ntiles + kXcds - 1) / kXcds;
   const int end = min(ntiles, (xcd + 1) * chunk);
-  int tile = xcd * chunk + slot;
-  if (tile >= end) return;
+  const int begin = xcd * chunk + slot;
+  if (begin >= end) return;
 
-  // Vector memory operations complete in issue order.  Every tile's first two k-stages
-  // are issued before the previous tile's 32 stores, so waiting until at most 32
-  // operations are outstanding leaves those stores draining while the tile computes.
-  // The first tile follows 32 stores that point past the end of the output (dropped),
-  // so the count is the same for every tile.
-  const __amdgpu_buffer_rsrc_t out0 =
-      __builtin_amdgcn_make_buffer_rsrc(Cw, (short)0, (int)out_bytes, 0x00020000);
   const uint32_t lo_f[2] = {lds0 + kouter_lane_off(lane, 0), lds0 + kouter_lane_off(lane, 1)};
-  const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-
-  TnTile t = tn_tile(tile, mtn, ntn, offsets);
-  TnLoader al, bl;
-  tn_setup(al, A, R, M, t.i0, lane);
-  tn_setup(bl, B, brows, N, t.n0, lane);
-  int rB2[4];  // B rows of stage 2 (gather indices fetched ahead)
-  tn_prefetch(t, al, bl, wv, lane, lds0, M, N, gather, rB2);
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int q = 0; q < kTnStores; ++q)  // distinct addresses, so none is merged away
-    __builtin_amdgcn_raw_buffer_store_b128(zero4, out0, out_bytes + 16u * q, 0, 0);
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mi][n][i] = 0.0f;
 
+  // tiles of groups without rows before the first stage: zeros, before any load
+  TnCursor c;
+  c.q = 0;
+  for (int t = begin; t < end; t += step) {
+    tn_tile_params(c, t, mtn, ntn, s_off);
+    if (c.nk > 0) break;
+    tn_store(Cw, acc, c.g, c.i0, c.n0, M, N, wm, wn, lane, smem, wv, true);
+    c.tile = end;
+  }
+  if (c.tile >= end || c.nk == 0) return;
+  TnCursor d = c, x = c;
+
+  // prologue: indices of the first kTAhead stages, then kTAhead steps of loads
+  if (kGather) {
+    for (int k = 0; k < kTAhead; ++k) {
+      tn_issue_index<kGather>(x, x.tile < end, grs, lds_idx, lane);
+      tn_advance(x, end, step, mtn, ntn, s_off);
+    }
+    wait_vm<0>();
+    __syncthreads();
+  }
+  for (int k = 0; k < kTAhead; ++k) {
+    tn_issue_index<kGather>(x, x.tile < end, grs, lds_idx, lane);
+    tn_advance(x, end, step, mtn, ntn, s_off);
+    tn_issue_stage<kGather>(d, d.tile < end, ars, brs, lds0, s_idx, wv, lane, M, N);
+    tn_advance(d, end, step, mtn, ntn, s_off);
+  }
+
+  int h0 = 0, h1 = 0, h2 = 0;  // store batches issued at the ends of the last 3 steps
   for (;;) {
-    f32x16 acc[2][4];
+    tn_wait<kGather>(h0 + h1 + h2);
+    __syncthreads();
+    // refill the buffer computed at the previous step
+    tn_issue_index<kGather>(x, x.tile < end, grs, lds_idx, lane);
+    tn_advance(x, end, step, mtn, ntn, s_off);
+    tn_issue_stage<kGather>(d, d.tile < end, ars, brs, lds0, s_idx, wv, lane, M, N);
+    tn_advance(d, end, step, mtn, ntn, s_off);
+
+    const uint32_t aoff = (c.q % kTRing) * 2 * kTOp + wm * 128;
+    const uint32_t boff = (c.q % kTRing) * 2 * kTOp + kTOp + 2 * wn * 128;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int s = 0; s < kTK / 16; ++s) {
+      bf16x8 b[4];
 #pragma unroll
       for (int n = 0; n < 4; ++n)
+        b[n] = frag_ko(lo_f[n & 1] + boff + (n >> 1) * 128 + s * 16 * kORow);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mi][n][i] = 0.0f;
-
-    for (int kt = 0; kt < t.nk; ++kt) {
-      if (kt < 2) wait_vm<kTnStores>();
-      else wait_vm<0>();
-      __syncthreads();
-      if (kt >= 1 && kt + 1 < t.nk) {  // stage kt+1 >= 2 into the buffer stage kt-1 used
-        const uint32_t sb = lds0 + ((kt + 1) & 1) * 2 * kOStage;
-        int ra[4], rb[4];
-        tn_rows(wv, lane, (kt + 1) * BK, t.m_g, t.row0, nullptr, ra);
-        if (kt == 1) {
+      for (int mi = 0; mi < 2; ++mi) {
+        const bf16x8 a = frag_ko(lo_f[mi] + aoff + s * 16 * kORow);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) rb[j] = rB2[j];
-        } else {
-          tn_rows(wv, lane, (kt + 1) * BK, t.m_g, t.row0, gather, rb);
-          wait_vm<0>();  // only these index reads are outstanding here
-        }
-        tn_issue(al, sb, wv, M, ra);
-        tn_issue(bl, sb + kOStage, wv, N, rb);
+        for (int n = 0; n < 4; ++n)  // output row = A column, 4 consecutive n per lane
+          acc[mi][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[n], a, acc[mi][n], 0, 0, 0);
       }
-      const uint32_t aoff = (kt & 1) * 2 * kOStage + wm * 128;
-      const uint32_t boff = (kt & 1) * 2 * kOStage + kOStage + 2 * wn * 128;
+    }
+
+    int batches = 0;
+    if (c.kt + 1 == c.nk) {  // last stage of the tile
+      // its buffer is free once every wave has computed it (it is refilled only after
+      // the next step's barrier): stage the output through it
+      __syncthreads();
+      tn_store(Cw, acc, c.g, c.i0, c.n0, M, N, wm, wn, lane,
+               smem + (c.q % kTRing) * 2 * kTOp, wv, false);
+      ++batches;
 #pragma unroll
-      for (int s = 0; s < BK / 16; ++s) {
-        bf16x8 b[4];
+      for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int n = 0; n < 4; ++n)
-          b[n] = frag_ko(lo_f[n & 1] + boff + (n >> 1) * 128 + s * 16 * kORow);
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-          const bf16x8 a = frag_ko(lo_f[mi] + aoff + s * 16 * kORow);
-#pragma unroll
-          for (int n = 0; n < 4; ++n)  // output row = A column, 4 consecutive n per lane
-            acc[mi][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[n], a, acc[mi][n], 0, 0, 0);
-        }
+          for (int i = 0; i < 16; ++i) acc[mi][n][i] = 0.0f;
+      // following tiles of groups without rows: zeros
+      int t = c.tile + step;
+      for (; t < end; t += step) {
+        tn_tile_params(c, t, mtn, ntn, s_off);
+        if (c.nk > 0) break;
+        tn_store(Cw, acc, c.g, c.i0, c.n0, M, N, wm, wn, lane, smem, wv, true);
+        ++batches;
       }
+      if (t >= end) {
+        wait_vm<0>();  // no load into LDS may outlive the workgroup
+        break;
+      }
+      ++c.q;
+    } else {
+      ++c.q;
+      ++c.kt;
     }
-
-    // the next tile: its rows, then (LDS free) its first two stages
-    const int next = tile + per_xcd;
-    const bool has_next = next < end;
-    const TnTile cur = t;
-    __syncthreads();  // every wave is done with this tile's LDS
-    if (has_next) {
-      t = tn_tile(next, mtn, ntn, offsets);
-      tn_setup(al, A, R, M, t.i0, lane);
-      tn_setup(bl, B, brows, N, t.n0, lane);
-      tn_prefetch(t, al, bl, wv, lane, lds0, M, N, gather, rB2);
-    }
-
-    // this tile's stores: lane holds output row i (its MFMA column) and 4 consecutive n
-    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-        Cw + (int64_t)cur.g * M * N, (short)0, (int)out_bytes, 0x00020000);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      const int row = cur.i0 + 64 * wm + 32 * mi + (lane & 31);
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = cur.n0 + 128 * wn + 32 * n + 8 * j + 4 * (lane >> 5);
-          const uint32_t off = (row < M && col < N)
-                                   ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 4u
-                                   : out_bytes;  // past the end: dropped
-          const f32x4 v = {acc[mi][n][4 * j], acc[mi][n][4 * j + 1], acc[mi][n][4 * j + 2],
-                           acc[mi][n][4 * j + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(v, crs, off, 0, 0);
-        }
-    }
-    if (!has_next) break;
-    tile = next;
+    h2 = h1;
+    h1 = h0;
+    h0 = batches;
   }
 }
 
@@ -611,15 +669,20 @@ hipError_t launch_ffn_bwd_weight(const Dims& d, const void* x, const int32_t* ga
   if (d.expert == MOE_BF16) {
     const int grid = bwd_grid(device_cu_count());
     // dW2 = dY^T h
-    hipLaunchKernelGGL(k_gemm_tn_bf16, dim3(grid), dim3(512), 0, st,
+    hipLaunchKernelGGL(k_gemm_tn_bf16<false>, dim3(grid), dim3(512), 0, st,
                        static_cast<const uint16_t*>(dys), static_cast<const uint16_t*>(h),
                        nullptr, R, dw2, offsets, NG, H, I);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // dW13 = [da|du]^T x
-    hipLaunchKernelGGL(k_gemm_tn_bf16, dim3(grid), dim3(512), 0, st,
-                       static_cast<const uint16_t*>(dau), static_cast<const uint16_t*>(x),
-                       gather, gather ? d.T : R, dw13, offsets, NG, 2 * I, H);
+    if (gather)
+      hipLaunchKernelGGL(k_gemm_tn_bf16<true>, dim3(grid), dim3(512), 0, st,
+                         static_cast<const uint16_t*>(dau), static_cast<const uint16_t*>(x),
+                         gather, d.T, dw13, offsets, NG, 2 * I, H);
+    else
+      hipLaunchKernelGGL(k_gemm_tn_bf16<false>, dim3(grid), dim3(512), 0, st,
+                         static_cast<const uint16_t*>(dau), static_cast<const uint16_t*>(x),
+                         nullptr, R, dw13, offsets, NG, 2 * I, H);
     return hipGetLastError();
   }
   if (d.expert == MOE_F32) {

@@ -42,6 +42,12 @@ __device__ __forceinline__ void load16_to_lds(i32x4 rsrc, uint32_t lds, uint32_t
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                ::"s"(lds), "v"(voff), "s"(rsrc) : "memory");
 }
+// Same, non-temporal: for data read once (expert weights streamed through a GEMM),
+// so it does not push reused rows out of the L2.
+__device__ __forceinline__ void load16_to_lds_nt(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               ::"s"(lds), "v"(voff), "s"(rsrc) : "memory");
+}
 __device__ __forceinline__ void load4_to_lds(i32x4 rsrc, uint32_t lds, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                ::"s"(lds), "v"(voff), "s"(rsrc) : "memory");

@@ -128,7 +128,10 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
 //   - 64-deep k steps: every row of a step is one full 128-byte line (narrower row
 //     segments cost far more memory-pipeline time per byte on this GPU).
 // Operands go from memory straight into LDS (buffer loads with the LDS destination
-// bit, no register staging).  The LDS ring is shaped per tile: the A stage holds
+// bit, no register staging).  Weight loads and output stores are non-temporal: a
+// weight tile is read only by the few workgroups working on it at the same moment and
+// outputs are not read again here, so the L2 is left to the activation rows that
+// every column tile of an expert re-reads.  The LDS ring is shaped per tile: the A stage holds
 // ceil(rows/64)*64 rows, and when a stage fits three times into 144 KiB (experts of
 // <= 128 rows) two steps are in flight while one is multiplied, else one.
 // Activation rows past the expert's end are read through a buffer descriptor sized
@@ -232,10 +235,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
     if (nA > 1) load16_to_lds(arsrc, sa_ + 64 * kRowBytes, aoff[1] + ko_);              \
     if (nA > 2) load16_to_lds(arsrc, sa_ + 128 * kRowBytes, aoff[2] + ko_);             \
     if (nA > 3) load16_to_lds(arsrc, sa_ + 192 * kRowBytes, aoff[3] + ko_);             \
-    load16_to_lds(brsrc, sa_ + sA, boff[0] + ko_);                                      \
-    load16_to_lds(brsrc, sa_ + sA + 64 * kRowBytes, boff[1] + ko_);                     \
-    load16_to_lds(brsrc, sa_ + sA + 128 * kRowBytes, boff[2] + ko_);                    \
-    load16_to_lds(brsrc, sa_ + sA + 192 * kRowBytes, boff[3] + ko_);                    \
+    load16_to_lds_nt(brsrc, sa_ + sA, boff[0] + ko_);                                      \
+    load16_to_lds_nt(brsrc, sa_ + sA + 64 * kRowBytes, boff[1] + ko_);                     \
+    load16_to_lds_nt(brsrc, sa_ + sA + 128 * kRowBytes, boff[2] + ko_);                    \
+    load16_to_lds_nt(brsrc, sa_ + sA + 192 * kRowBytes, boff[3] + ko_);                    \
   }
 
     f32x16 acc[2][4];
@@ -304,7 +307,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
               const int col = tl.n_idx * 128 + 64 * wn + 32 * t + (lane & 31);
-              cp[col] = f32_to_bf16_bits(silu(acc[mi][2 * t][i]) * acc[mi][2 * t + 1][i]);
+              __builtin_nontemporal_store(
+                  f32_to_bf16_bits(silu(acc[mi][2 * t][i]) * acc[mi][2 * t + 1][i]), cp + col);
               if (au) {  // gate and up pre-activations, kept for the backward
                 uint16_t* ap = au + (int64_t)(row0 + m0 + m) * 2 * half;
                 ap[col] = f32_to_bf16_bits(acc[mi][2 * t][i]);
@@ -314,7 +318,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
           } else {
 #pragma unroll
             for (int n = 0; n < 4; ++n)
-              cp[tl.n_idx * BN + 128 * wn + 32 * n + (lane & 31)] = f32_to_bf16_bits(acc[mi][n][i]);
+              __builtin_nontemporal_store(f32_to_bf16_bits(acc[mi][n][i]),
+                                          cp + tl.n_idx * BN + 128 * wn + 32 * n + (lane & 31));
           }
         }
     }

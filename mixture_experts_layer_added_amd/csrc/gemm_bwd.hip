@@ -309,6 +309,7 @@ constexpr int kTRing = 4;              // stages held in LDS
 constexpr int kTAhead = 3;             // stages in flight ahead of the one computed
 constexpr int kTIdx = 8;               // gather-index slots of 64 ints (> kTAhead)
 constexpr int kTStores = 32;           // 16-byte stores per lane per tile
+constexpr int kCpolNT = 2;             // cache-policy bit of a buffer store: non-temporal
 static_assert(kTAhead < kTRing, "the buffer refilled at a step was computed the step before");
 
 struct TnCursor {
@@ -433,7 +434,9 @@ __device__ __forceinline__ void tn_store(float* __restrict__ Cw, const f32x16 (&
         const uint32_t off = (row < M && col < N)
                                  ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 4u
                                  : out_bytes;  // past the end: dropped
-        __builtin_amdgcn_raw_buffer_store_b128(v, crs, off, 0, 0);
+        // non-temporal: the gradient is not read again here, and keeping it out of the
+        // L2 keeps the operand rows there
+        __builtin_amdgcn_raw_buffer_store_b128(v, crs, off, 0, kCpolNT);
       }
     }
 }

@@ -152,10 +152,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(
     if (nA > 1) load16_to_lds(arsrc, sa_ + 64 * FBK, aoff[1] + ko_);                  \
     if (nA > 2) load16_to_lds(arsrc, sa_ + 128 * FBK, aoff[2] + ko_);                 \
     if (nA > 3) load16_to_lds(arsrc, sa_ + 192 * FBK, aoff[3] + ko_);                 \
-    load16_to_lds(brsrc, sa_ + sA, boff[0] + ko_);                                    \
-    load16_to_lds(brsrc, sa_ + sA + 64 * FBK, boff[1] + ko_);                         \
-    load16_to_lds(brsrc, sa_ + sA + 128 * FBK, boff[2] + ko_);                        \
-    load16_to_lds(brsrc, sa_ + sA + 192 * FBK, boff[3] + ko_);                        \
+    load16_to_lds_nt(brsrc, sa_ + sA, boff[0] + ko_);                                    \
+    load16_to_lds_nt(brsrc, sa_ + sA + 64 * FBK, boff[1] + ko_);                         \
+    load16_to_lds_nt(brsrc, sa_ + sA + 128 * FBK, boff[2] + ko_);                        \
+    load16_to_lds_nt(brsrc, sa_ + sA + 192 * FBK, boff[3] + ko_);                        \
     if (ld_sa) load4_to_lds(srsrc, ldss + (st) * (FBM * 4), soff + (uint32_t)(kt) * 4); \
   }
 
@@ -249,7 +249,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(
           uint8_t* hp = hq + (int64_t)(row0 + m0 + r) * Nout + n_idx * 128 + (lane & 31);
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            hp[32 * t] = static_cast<uint8_t>(f32_to_e4m3_bits(hv[t][i] / sc));
+            __builtin_nontemporal_store(static_cast<uint8_t>(f32_to_e4m3_bits(hv[t][i] / sc)),
+                                        hp + 32 * t);
           if ((lane & 31) == 0) C_scale[(int64_t)(row0 + m0 + r) * ncb + n_idx] = sc;
         }
       }
@@ -262,7 +263,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(
         uint16_t* yp = y + (int64_t)(row0 + m0 + r) * Nout + n_idx * FBN + (lane & 31);
 #pragma unroll
         for (int n = 0; n < 8; ++n)
-          if (n_idx * FBN + 32 * n < Nout) yp[32 * n] = f32_to_bf16_bits(acc[n][i]);
+          if (n_idx * FBN + 32 * n < Nout)  // non-temporal, as the weight loads
+            __builtin_nontemporal_store(f32_to_bf16_bits(acc[n][i]), yp + 32 * n);
       }
     }
   }

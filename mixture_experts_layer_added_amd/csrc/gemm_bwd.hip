@@ -72,8 +72,9 @@ __device__ __forceinline__ bf16x8 frag_ko(uint32_t addr) {
   return f;
 }
 
-// One k-stage of a K-outer operand: k-rows k0 .. k0+63 (those >= krows read as zeros)
-// of columns col0 .. col0+255 (those >= ncols read as zeros) of a row-major matrix
+// One k-stage of a K-outer operand (the weights of the dgrad GEMMs, loaded
+// non-temporally: each weight tile is streamed once): k-rows k0 .. k0+63 (those >=
+// krows read as zeros) of columns col0 .. col0+255 (those >= ncols read as zeros) of a row-major matrix
 // with `ld` elements per row.  Wave wv, instruction j fills k-rows 2(4wv+j), +1.
 // gather != nullptr: k-row q is matrix row gather[q].
 struct KOuterLoader {
@@ -109,7 +110,7 @@ __device__ __forceinline__ void kouter_issue(const KOuterLoader& L, uint32_t lds
       const int grow = gather ? gather[rowbase + kr] : rowbase + kr;
       voff = (uint32_t)grow * (uint32_t)ld * 2u + L.off[j];
     }
-    load16_to_lds(L.rsrc, lds_stage + (4 * wv + j) * 1024, voff);
+    load16_to_lds_nt(L.rsrc, lds_stage + (4 * wv + j) * 1024, voff);  // weights: streamed
   }
 }
 
@@ -270,10 +271,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nn_bf16(
               const float a = bf16_bits_to_f32(au[r * 2 * I + col]);
               const float u = bf16_bits_to_f32(au[r * 2 * I + I + col]);
               const float sg = 1.0f / (1.0f + __expf(-a));
-              C[r * 2 * I + col] = f32_to_bf16_bits(dh * u * (sg * (1.0f + a * (1.0f - sg))));
-              C[r * 2 * I + I + col] = f32_to_bf16_bits(dh * (a * sg));
+              __builtin_nontemporal_store(
+                  f32_to_bf16_bits(dh * u * (sg * (1.0f + a * (1.0f - sg)))), C + r * 2 * I + col);
+              __builtin_nontemporal_store(f32_to_bf16_bits(dh * (a * sg)), C + r * 2 * I + I + col);
             } else {
-              C[r * N + col] = f32_to_bf16_bits(dh);
+              __builtin_nontemporal_store(f32_to_bf16_bits(dh), C + r * N + col);
             }
           }
         }

@@ -41,23 +41,19 @@ __device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)
 // K-inner operand (rows of 128 B): chunk slots xor-swizzled by (row >> 1) & 7.
 __device__ __forceinline__ int swz_a(int r, int c) { return r * kARow + ((c ^ (r >> 1)) & 7) * 16; }
 
-// K-outer operand (k-rows of 512 B = 32 chunks): chunk c of k-row r sits in slot
-// c ^ (2 (r & 3)), so the 4 k-rows x 2 chunks a 16-lane transposed read touches land
-// in 8 distinct bank groups.
-__device__ __forceinline__ int swz_o(int r, int c) { return r * kORow + ((c ^ (2 * (r & 3))) << 4); }
-
-// Lane part of the LDS byte offset of a K-outer fragment read, for fragment columns
-// nb with (nb / 32) & 1 == par.  In each 16-lane group g, source lane j reads k-row
-// 8 (g >> 1) + j / 4 and 4 columns starting at 16 (g & 1) + 4 (j & 3); the chunk swizzle
-// stays inside an aligned group of 8 chunks (64 columns), so the fragment at columns
-// nb, k-step s (16 k-rows), upper half (k + 4) sits at
-//   kouter_lane_off(lane, par) + (nb / 64) * 128 + s * 8192 + hi * 2048,
+// K-outer stages keep k-rows of 512 bytes (256 columns) with 16-byte chunk c of k-row r
+// at slot c ^ 4 (r & 3).  In each 16-lane group g of a fragment read
+// (ds_read_b64_tr_b16), source lane j reads k-row 8 (g >> 1) + j / 4 and 4 columns
+// from 16 (g & 1) + 4 (j & 3), so a half-wave touches 4 k-rows x 4 chunks = 16 distinct
+// slots of a 256-byte bank window.  For fragment columns nb with (nb / 32) & 3 == p the
+// read of k-step s (16 k-rows), half hi (k + 4) sits at
+//   tn_lane_off(lane, p) + (nb / 128) * 256 + s * 8192 + hi * 2048,
 // constants the compiler folds into the read's offset field.
-__device__ __forceinline__ uint32_t kouter_lane_off(int lane, int par) {
+__device__ __forceinline__ uint32_t tn_lane_off(int lane, int p) {
   const int g = lane >> 4, j = lane & 15, i = j >> 2;
   const int row = 8 * (g >> 1) + i;
-  const int c = 4 * par + 2 * (g & 1) + ((j & 3) >> 1);
-  return (uint32_t)(row * kORow + ((c ^ (2 * i)) << 4) + (j & 1) * 8);
+  const int c = 4 * p + 2 * (g & 1) + ((j & 3) >> 1);
+  return (uint32_t)(row * kORow + ((c ^ (4 * i)) << 4) + (j & 1) * 8);
 }
 
 // 8 consecutive k of one column per lane (the v_mfma_f32_32x32x16_bf16 operand layout)
@@ -91,7 +87,7 @@ __device__ __forceinline__ void kouter_setup(KOuterLoader& L, const void* base, 
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 2 * (4 * wv + j) + (lane >> 5);
-    const int c = slot ^ (2 * (r & 3));
+    const int c = slot ^ (4 * (r & 3));
     L.krow[j] = r;
     L.row_ok[j] = col0 + 8 * c < ncols;
     L.off[j] = (uint32_t)((col0 + 8 * c) * 2);
@@ -194,7 +190,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nn_bf16(
     KOuterLoader bl;
     kouter_setup(bl, B + (int64_t)tl.g * Kd * N, Kd, N, n0, N, lane, wv);
     const uint32_t ldsw = lds0 + 8 * wv * kARow;
-    const uint32_t lo_b[2] = {lds0 + kouter_lane_off(lane, 0), lds0 + kouter_lane_off(lane, 1)};
+    uint32_t lo_b[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) lo_b[p] = lds0 + tn_lane_off(lane, p);
 
 #define NN_STAGE_LOAD(kt, st)                                                         \
   {                                                                                   \
@@ -230,14 +228,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nn_bf16(
       }
       if (w_on) {
         const char* as = smem + st * sStage;
-        const uint32_t boff = st * sStage + sA + 2 * wn * 128;
+        const uint32_t boff = st * sStage + sA + wn * 256;
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
           const int c = 2 * s + kq;
           bf16x8 b[4];
 #pragma unroll
           for (int n = 0; n < 4; ++n)
-            b[n] = frag_ko(lo_b[n & 1] + boff + (n >> 1) * 128 + s * 16 * kORow);
+            b[n] = frag_ko(lo_b[n] + boff + s * 16 * kORow);
           const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(as + swz_a(arow0, c));
 #pragma unroll
           for (int n = 0; n < 4; ++n)
@@ -291,6 +289,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nn_bf16(
 //
 // With ~128 rows per expert a tile is little MFMA work and 256 KiB of fp32 output, so
 // the kernel is bound by HBM writes, and the loads must not wait behind the stores.
+//  * Stage k-rows are 512 bytes (256 columns) with 16-byte chunk c of k-row r at slot
+//    c ^ 4 (r & 3): the 32 lanes of a half-wave fragment read (4 k-rows x 4 chunks)
+//    touch 16 distinct slots of a 256-byte bank window.
 //  * The k-stages (32 rows of both operands, 32 KiB) of all the workgroup's tiles form
 //    one stream: stage q is loaded kTAhead steps before it is computed, into LDS buffer
 //    q % kTRing, across tile boundaries.  With gather, the 32 row indices of stage q
@@ -355,8 +356,9 @@ __device__ __forceinline__ void tn_advance(TnCursor& c, int end, int step, int m
 // 16 bytes for load instruction j; k-row of instruction j is 2 (2 wv + j) + lane / 32.
 __device__ __forceinline__ int tn_chunk(int j, int lane) {
   const int r = 2 * j + (lane >> 5);  // k-row mod 4
-  return (lane & 31) ^ (2 * (r & 3));
+  return (lane & 31) ^ (4 * (r & 3));
 }
+
 
 // the 32 gather indices of stage x into its 256-byte slot (lanes 32-63 fill the upper
 // half of the slot with zeros)
@@ -472,7 +474,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tn_bf16(
   const int begin = xcd * chunk + slot;
   if (begin >= end) return;
 
-  const uint32_t lo_f[2] = {lds0 + kouter_lane_off(lane, 0), lds0 + kouter_lane_off(lane, 1)};
+  uint32_t lo4[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) lo4[p] = lds0 + tn_lane_off(lane, p);
+  const uint32_t la0 = ((wm & 1) ? lo4[2] : lo4[0]) + (wm >> 1) * 256;
+  const uint32_t la1 = ((wm & 1) ? lo4[3] : lo4[1]) + (wm >> 1) * 256;
   f32x16 acc[2][4];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
@@ -519,17 +525,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tn_bf16(
     tn_issue_stage<kGather>(d, d.tile < end, ars, brs, lds0, s_idx, wv, lane, M, N);
     tn_advance(d, end, step, mtn, ntn, s_off);
 
-    const uint32_t aoff = (c.q % kTRing) * 2 * kTOp + wm * 128;
-    const uint32_t boff = (c.q % kTRing) * 2 * kTOp + kTOp + 2 * wn * 128;
+    const uint32_t aoff = (c.q % kTRing) * 2 * kTOp;
+    const uint32_t boff = (c.q % kTRing) * 2 * kTOp + kTOp + wn * 256;
 #pragma unroll
     for (int s = 0; s < kTK / 16; ++s) {
       bf16x8 b[4];
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
-        b[n] = frag_ko(lo_f[n & 1] + boff + (n >> 1) * 128 + s * 16 * kORow);
+      for (int n = 0; n < 4; ++n) b[n] = frag_ko(lo4[n] + boff + s * 16 * kORow);
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
-        const bf16x8 a = frag_ko(lo_f[mi] + aoff + s * 16 * kORow);
+        const bf16x8 a = frag_ko((mi ? la1 : la0) + aoff + s * 16 * kORow);
 #pragma unroll
         for (int n = 0; n < 4; ++n)  // output row = A column, 4 consecutive n per lane
           acc[mi][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[n], a, acc[mi][n], 0, 0, 0);

@@ -244,7 +244,8 @@ def main():
         NG = E + w.S
         cb_bytes = T * H * a + T * K * H * a + R * H * a + T * K * 12
         rb_bytes = T * K * 12 + 2 * E * H * 4 + T * H * 4 + T * K * H * a
-        bi_bytes = (R * H * a + touched * H * I * es + R * 2 * I * a * 2
+        # dh GEMM: dY, au in, dau out; dx GEMM: dau in, dx_sorted out
+        bi_bytes = (R * H * a + touched * H * I * es + R * 2 * I * a * 3
                     + touched * 2 * I * H * es + R * H * a)
         bi_flops = 2.0 * R * H * I + 2.0 * R * 2 * I * H
         x_rows = R if args.materialize else T

@@ -14,54 +14,73 @@
 namespace moe {
 namespace {
 
-// One workgroup per (token, 2048-column slice); each thread owns 16 bytes of the row.
+constexpr int kMaxK = 16;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt(void* p, const uint4& o) {
+  const u32x4 v = {o.x, o.y, o.z, o.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void k_combine(const T* __restrict__ ys,
+__device__ __forceinline__ void widen(const uint4& u, float* v) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+    v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+  }
+}
+
+// One workgroup of 128 threads per (token, 128 chunks of 16 bytes); each thread owns 16
+// bytes of the row.  All K+1 rows are loaded before the first multiply-add (the loads are
+// independent, so they are all in flight together), then summed in rank order.  Y is
+// read once and y is not read again here: both go non-temporal.
+template <typename T>
+__global__ __launch_bounds__(128) void k_combine(const T* __restrict__ ys,
                                                  const int32_t* __restrict__ inv_perm,
                                                  const float* __restrict__ gate, T* __restrict__ y,
                                                  int Tn, int H, int K, int S) {
   constexpr int V = 16 / sizeof(T);
   const int t = blockIdx.x;
-  const int c = blockIdx.y * 256 + threadIdx.x;
+  const int c = blockIdx.y * 128 + threadIdx.x;
   if (c * V >= H) return;
+  uint4 u[kMaxK];
+  int row[kMaxK];
+#pragma unroll
+  for (int k = 0; k < kMaxK; ++k) {
+    row[k] = k < K ? inv_perm[(int64_t)t * K + k] : -1;
+    if (row[k] >= 0)
+      u[k] = ld_nt(ys + (int64_t)row[k] * H + c * V);
+  }
+  uint4 us = make_uint4(0, 0, 0, 0);
+  if (S) us = ld_nt(ys + ((int64_t)Tn * K + t) * H + c * V);
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.0f;
-  for (int k = 0; k < K; ++k) {
-    const int row = inv_perm[(int64_t)t * K + k];
+#pragma unroll
+  for (int k = 0; k < kMaxK; ++k) {
+    if (row[k] < 0) continue;
     const float g = gate[(int64_t)t * K + k];
-    if (row < 0) continue;
-    const uint4 u = *reinterpret_cast<const uint4*>(ys + (int64_t)row * H + c * V);
-    if constexpr (sizeof(T) == 2) {
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    float v[V];
+    widen<T>(u[k], v);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = __builtin_fmaf(g, __uint_as_float(w[i] << 16), acc[2 * i]);
-        acc[2 * i + 1] = __builtin_fmaf(g, __uint_as_float(w[i] & 0xFFFF0000u), acc[2 * i + 1]);
-      }
-    } else {
-      const float w[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
-                          __uint_as_float(u.w)};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(g, w[i], acc[i]);
-    }
+    for (int i = 0; i < V; ++i) acc[i] = __builtin_fmaf(g, v[i], acc[i]);
   }
   if (S) {
-    const int64_t row = (int64_t)Tn * K + t;
-    const uint4 u = *reinterpret_cast<const uint4*>(ys + row * H + c * V);
-    if constexpr (sizeof(T) == 2) {
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    float v[V];
+    widen<T>(us, v);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = __uint_as_float(w[i] << 16) + acc[2 * i];
-        acc[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) + acc[2 * i + 1];
-      }
-    } else {
-      acc[0] = __uint_as_float(u.x) + acc[0];
-      acc[1] = __uint_as_float(u.y) + acc[1];
-      acc[2] = __uint_as_float(u.z) + acc[2];
-      acc[3] = __uint_as_float(u.w) + acc[3];
-    }
+    for (int i = 0; i < V; ++i) acc[i] = v[i] + acc[i];
   }
   uint4 o;
   if constexpr (sizeof(T) == 2) {
@@ -75,7 +94,7 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ ys,
     o.z = __float_as_uint(acc[2]);
     o.w = __float_as_uint(acc[3]);
   }
-  *reinterpret_cast<uint4*>(y + (int64_t)t * H + c * V) = o;
+  st_nt(y + (int64_t)t * H + c * V, o);
 }
 
 __global__ void k_bias_update(const int32_t* __restrict__ counts, float* __restrict__ bias,
@@ -138,13 +157,13 @@ hipError_t launch_combine(const Dims& d, const void* ys, const int32_t* inv_perm
                           const float* gate, void* y, hipStream_t st) {
   const int T = static_cast<int>(d.T);
   if (d.act == MOE_BF16) {
-    dim3 grid(T, (d.H / 8 + 255) / 256);
-    hipLaunchKernelGGL(k_combine<uint16_t>, grid, dim3(256), 0, st,
+    dim3 grid(T, (d.H / 8 + 127) / 128);
+    hipLaunchKernelGGL(k_combine<uint16_t>, grid, dim3(128), 0, st,
                        static_cast<const uint16_t*>(ys), inv_perm, gate,
                        static_cast<uint16_t*>(y), T, d.H, d.K, d.S);
   } else {
-    dim3 grid(T, (d.H / 4 + 255) / 256);
-    hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), 0, st, static_cast<const float*>(ys),
+    dim3 grid(T, (d.H / 4 + 127) / 128);
+    hipLaunchKernelGGL(k_combine<float>, grid, dim3(128), 0, st, static_cast<const float*>(ys),
                        inv_perm, gate, static_cast<float*>(y), T, d.H, d.K, d.S);
   }
   return hipGetLastError();

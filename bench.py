@@ -91,6 +91,9 @@ def parse():
     ap.add_argument("--materialize", action="store_true",
                     help="permute writes x_sorted and the gate/up GEMM reads it (default: the "
                          "GEMM gathers its rows from x)")
+    ap.add_argument("--route-only", action="store_true",
+                    help="time moe_route alone (router logits + group-limited top-K); with "
+                         "--tokens it runs at batch sizes whose expert FFN buffers would not fit")
     ap.add_argument("--train", action="store_true",
                     help="time forward + bias update + backward (bf16 / fp32 experts)")
     ap.add_argument("--cpu-ffn-rows", type=int, default=0,
@@ -123,6 +126,8 @@ def main():
     w = workloads.get(args.workload)
     if args.tokens:
         w = workloads.get(args.workload, T=args.tokens)
+    if args.route_only:
+        return route_only(args, w, dev)
     log(f"[bench] workload {w.name} T={w.T} H={w.H} E={w.E} K={w.K} I={w.I} expert={w.expert}")
 
     t0 = time.time()
@@ -316,6 +321,62 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "experts_touched": touched,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def route_only(args, w, dev):
+    """moe_route alone: logits (fp32 VALU, fixed order) then the selection kernel."""
+    import torch
+
+    import workloads
+    from mixture_experts_layer_added_amd import _lib as L
+
+    w_router, bias = workloads.make_router(w, dev)
+    x = workloads.make_x(w, device=dev)
+    p = L.problem(w.T, w.H, w.E, w.G, w.M, w.K, w.J, w.I, w.S,
+                  L.MOE_BF16 if w.act == "bf16" else L.MOE_F32,
+                  L.MOE_BF16 if w.act == "bf16" else L.MOE_F32)
+    idx = torch.empty((w.T, w.K), dtype=torch.int32, device=dev)
+    gate = torch.empty((w.T, w.K), dtype=torch.float32, device=dev)
+    counts = torch.empty((w.E,), dtype=torch.int32, device=dev)
+    logits = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
+    n = L.moe_workspace_bytes(p, L.MOE_CALL_ROUTE)
+    ws = torch.empty((max(n, 256),), dtype=torch.uint8, device=dev)
+
+    def step():
+        L.moe_route(p, x, w_router, bias, idx, gate, counts, logits, ws, ws.numel())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+    flops = 2.0 * w.T * w.E * w.H
+    tfs = flops / (ms * 1e-3) / 1e12
+    a = 2 if w.act == "bf16" else 4
+    out = {
+        "metric": "MoE router tokens/s (route only: fp32 logits + group-limited top-K)",
+        "value": round(w.T * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded; x N(0,1), router weight N(0,0.02))",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "G": w.G, "M": w.M,
+                   "K": w.K, "J": w.J, "act": w.act, "step": "route only",
+                   "parallelism": "single GPU"},
+        # the whole call is timed; the logits kernel dominates it (VALU-bound)
+        "roofline": {"kernel": "moe_route (k_router_logits dominates)", "bound": "alu",
+                     "achieved": round(tfs, 2), "peak": VALU_FP32_PEAK, "unit": "TFLOP/s",
+                     "frac": round(tfs / VALU_FP32_PEAK, 4), "traffic": None},
+        "cpu_baseline": None,
+        # algorithmic bytes of the selection kernel (logits row + bias in, indices and
+        # gates out); its duration comes from a kernel trace of this run
+        "select_bytes": w.T * (w.E * 4 + w.K * 8) + 2 * w.E * 4,
+        "logits_bytes": w.T * w.H * a + w.E * w.H * 4 + w.T * w.E * 4,
     }
     print(json.dumps(out), flush=True)
 

@@ -147,13 +147,14 @@ __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib)
 // K rounds of a wave-wide (key, index) argmax over the kept groups pick the experts
 // in rank order.
 // ---------------------------------------------------------------------------
-constexpr int kMaxE = 512, kMaxPer = kMaxE / kWave, kMaxJ = 8, kMaxG = 64;
+constexpr int kMaxE = 512, kMaxPer = kMaxE / kWave, kMaxG = 64;
 
+template <int kJ>
 __global__ __launch_bounds__(256) void k_router_select(const float* __restrict__ z,
                                                        const float* __restrict__ bias,
                                                        int32_t* __restrict__ idx, float* __restrict__ gate,
                                                        int32_t* __restrict__ counts, int T, int E, int G,
-                                                       int M, int K, int J) {
+                                                       int M, int K) {
   __shared__ float s_key[4][kMaxE];
   __shared__ float s_aff[4][kMaxE];
   __shared__ float s_gscore[4][kMaxG];
@@ -182,10 +183,10 @@ __global__ __launch_bounds__(256) void k_router_select(const float* __restrict__
   if (lane < G) {
     // ordered list of the best keys so far, kept by carrying each new key down the
     // list and swapping where it ranks first (static indices: stays in registers)
-    float top[kMaxJ];
-    int topi[kMaxJ];
+    float top[kJ];
+    int topi[kJ];
 #pragma unroll
-    for (int q = 0; q < kMaxJ; ++q) {
+    for (int q = 0; q < kJ; ++q) {
       top[q] = -__builtin_inff();
       topi[q] = 0x7FFFFFFF;
     }
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(256) void k_router_select(const float* __restrict__
       float v = s_key[wv][e];
       int vi = e;
 #pragma unroll
-      for (int q = 0; q < kMaxJ; ++q) {
+      for (int q = 0; q < kJ; ++q) {
         if (ranks_before(v, vi, top[q], topi[q])) {
           const float tv = top[q];
           const int ti = topi[q];
@@ -206,8 +207,7 @@ __global__ __launch_bounds__(256) void k_router_select(const float* __restrict__
     }
     float sc = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kMaxJ; ++q)
-      if (q < J) sc = sc + top[q];
+    for (int q = 0; q < kJ; ++q) sc = sc + top[q];
     s_gscore[wv][lane] = sc;
   }
   __syncthreads();
@@ -281,8 +281,18 @@ hipError_t launch_route(const Dims& d, const void* x, const float* w_router, con
                        static_cast<const float*>(x), w_router, logits, counts, T, d.H, d.E);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_router_select, dim3((T + 3) / 4), dim3(256), 0, st, logits, bias, idx,
-                     gate, counts, T, d.E, d.G, d.M, d.K, d.J);
+  // the group lists have exactly J entries (J <= 8)
+#define MOE_SELECT(J_)                                                                         \
+  case J_:                                                                                     \
+    hipLaunchKernelGGL(k_router_select<J_>, dim3((T + 3) / 4), dim3(256), 0, st, logits, bias, \
+                       idx, gate, counts, T, d.E, d.G, d.M, d.K);                              \
+    break;
+  switch (d.J) {
+    MOE_SELECT(1) MOE_SELECT(2) MOE_SELECT(3) MOE_SELECT(4)
+    MOE_SELECT(5) MOE_SELECT(6) MOE_SELECT(7) MOE_SELECT(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_SELECT
   return hipGetLastError();
 }
 

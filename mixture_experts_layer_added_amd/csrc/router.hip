@@ -145,7 +145,9 @@ __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib)
 // l, l+64, ... (at most 8).  Keys and affinities go to LDS; lane g < G ranks the
 // keys of group g and sums its J best; lane g then ranks its group among all G;
 // K rounds of a wave-wide (key, index) argmax over the kept groups pick the experts
-// in rank order.
+// in rank order.  Expert counts go to an LDS histogram per workgroup, added to the
+// global counts once at the end (at large batches the per-token global atomics on 256
+// addresses were the kernel's main cost).
 // ---------------------------------------------------------------------------
 constexpr int kMaxE = 512, kMaxPer = kMaxE / kWave, kMaxG = 64;
 
@@ -159,111 +161,122 @@ __global__ __launch_bounds__(256) void k_router_select(const float* __restrict__
   __shared__ float s_aff[4][kMaxE];
   __shared__ float s_gscore[4][kMaxG];
   __shared__ int s_kept[4][kMaxG];
+  __shared__ int s_cnt[kMaxE];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t_raw = blockIdx.x * 4 + wv;
-  const bool live = t_raw < T;
-  const int t = live ? t_raw : T - 1;
   const int gs = E / G;
   const int per = (E + kWave - 1) / kWave;
+  for (int e = threadIdx.x; e < E; e += 256) s_cnt[e] = 0;
+  // grid-stride over groups of 4 tokens (one per wave); the bounds are uniform over
+  // the workgroup, so every wave takes part in every barrier
+  for (int base = blockIdx.x * 4; base < T; base += gridDim.x * 4) {
+    const int t_raw = base + wv;
+    const bool live = t_raw < T;
+    const int t = live ? t_raw : T - 1;
+    __syncthreads();  // the previous token's LDS rows are no longer read
 
-  float key[kMaxPer];
-#pragma unroll
-  for (int i = 0; i < kMaxPer; ++i) {
-    key[i] = 0.0f;
-    const int e = lane + kWave * i;
-    if (i < per && e < E) {
-      const float s = affinity(z[(int64_t)t * E + e]);
-      key[i] = s + bias[e];
-      s_key[wv][e] = key[i];
-      s_aff[wv][e] = s;
+    float key[kMaxPer];
+  #pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      key[i] = 0.0f;
+      const int e = lane + kWave * i;
+      if (i < per && e < E) {
+        const float s = affinity(z[(int64_t)t * E + e]);
+        key[i] = s + bias[e];
+        s_key[wv][e] = key[i];
+        s_aff[wv][e] = s;
+      }
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  if (lane < G) {
-    // ordered list of the best keys so far, kept by carrying each new key down the
-    // list and swapping where it ranks first (static indices: stays in registers)
-    float top[kJ];
-    int topi[kJ];
-#pragma unroll
-    for (int q = 0; q < kJ; ++q) {
-      top[q] = -__builtin_inff();
-      topi[q] = 0x7FFFFFFF;
-    }
-    for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
-      float v = s_key[wv][e];
-      int vi = e;
-#pragma unroll
+    if (lane < G) {
+      // ordered list of the best keys so far, kept by carrying each new key down the
+      // list and swapping where it ranks first (static indices: stays in registers)
+      float top[kJ];
+      int topi[kJ];
+  #pragma unroll
       for (int q = 0; q < kJ; ++q) {
-        if (ranks_before(v, vi, top[q], topi[q])) {
-          const float tv = top[q];
-          const int ti = topi[q];
-          top[q] = v;
-          topi[q] = vi;
-          v = tv;
-          vi = ti;
+        top[q] = -__builtin_inff();
+        topi[q] = 0x7FFFFFFF;
+      }
+      for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
+        float v = s_key[wv][e];
+        int vi = e;
+  #pragma unroll
+        for (int q = 0; q < kJ; ++q) {
+          if (ranks_before(v, vi, top[q], topi[q])) {
+            const float tv = top[q];
+            const int ti = topi[q];
+            top[q] = v;
+            topi[q] = vi;
+            v = tv;
+            vi = ti;
+          }
         }
       }
+      float sc = 0.0f;
+  #pragma unroll
+      for (int q = 0; q < kJ; ++q) sc = sc + top[q];
+      s_gscore[wv][lane] = sc;
     }
-    float sc = 0.0f;
-#pragma unroll
-    for (int q = 0; q < kJ; ++q) sc = sc + top[q];
-    s_gscore[wv][lane] = sc;
-  }
-  __syncthreads();
-  if (lane < G) {
-    const float mine = s_gscore[wv][lane];
-    int rank = 0;
-    for (int g = 0; g < G; ++g)
-      rank += ranks_before(s_gscore[wv][g], g, mine, lane) ? 1 : 0;
-    s_kept[wv][lane] = rank < M;
-  }
-  __syncthreads();
+    __syncthreads();
+    if (lane < G) {
+      const float mine = s_gscore[wv][lane];
+      int rank = 0;
+      for (int g = 0; g < G; ++g)
+        rank += ranks_before(s_gscore[wv][g], g, mine, lane) ? 1 : 0;
+      s_kept[wv][lane] = rank < M;
+    }
+    __syncthreads();
 
-  bool avail[kMaxPer];
-#pragma unroll
-  for (int i = 0; i < kMaxPer; ++i) {
-    const int e = lane + kWave * i;
-    avail[i] = (i < per) && (e < E) && s_kept[wv][e / gs];
-  }
-  int my_e = 0;
-  float my_s = 0.0f;
-  for (int r = 0; r < K; ++r) {
-    float bv = -__builtin_inff();
-    int bi = 0x7FFFFFFF;
-#pragma unroll
+    bool avail[kMaxPer];
+  #pragma unroll
     for (int i = 0; i < kMaxPer; ++i) {
       const int e = lane + kWave * i;
-      if (avail[i] && ranks_before(key[i], e, bv, bi)) {
-        bv = key[i];
-        bi = e;
+      avail[i] = (i < per) && (e < E) && s_kept[wv][e / gs];
+    }
+    int my_e = 0;
+    float my_s = 0.0f;
+    for (int r = 0; r < K; ++r) {
+      float bv = -__builtin_inff();
+      int bi = 0x7FFFFFFF;
+  #pragma unroll
+      for (int i = 0; i < kMaxPer; ++i) {
+        const int e = lane + kWave * i;
+        if (avail[i] && ranks_before(key[i], e, bv, bi)) {
+          bv = key[i];
+          bi = e;
+        }
+      }
+  #pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (ranks_before(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if (bi >= E) bi = 0;  // unreachable: K <= M*E/G candidates always exist
+  #pragma unroll
+      for (int i = 0; i < kMaxPer; ++i)
+        if (bi == lane + kWave * i) avail[i] = false;
+      if (lane == r) {
+        my_e = bi;
+        my_s = s_aff[wv][bi];
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ranks_before(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (bi >= E) bi = 0;  // unreachable: K <= M*E/G candidates always exist
-#pragma unroll
-    for (int i = 0; i < kMaxPer; ++i)
-      if (bi == lane + kWave * i) avail[i] = false;
-    if (lane == r) {
-      my_e = bi;
-      my_s = s_aff[wv][bi];
+    float sum = 0.0f;
+    for (int r = 0; r < K; ++r) sum = sum + __shfl(my_s, r);
+    if (live && lane < K) {
+      idx[(int64_t)t * K + lane] = my_e;
+      gate[(int64_t)t * K + lane] = my_s / sum;
+      atomicAdd(&s_cnt[my_e], 1);
     }
   }
-  float sum = 0.0f;
-  for (int r = 0; r < K; ++r) sum = sum + __shfl(my_s, r);
-  if (live && lane < K) {
-    idx[(int64_t)t * K + lane] = my_e;
-    gate[(int64_t)t * K + lane] = my_s / sum;
-    atomicAdd(&counts[my_e], 1);
-  }
+  // one global addition per expert and workgroup (integer sums: order-free)
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256)
+    if (s_cnt[e]) atomicAdd(&counts[e], s_cnt[e]);
 }
 
 }  // namespace
@@ -281,11 +294,13 @@ hipError_t launch_route(const Dims& d, const void* x, const float* w_router, con
                        static_cast<const float*>(x), w_router, logits, counts, T, d.H, d.E);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // the group lists have exactly J entries (J <= 8)
-#define MOE_SELECT(J_)                                                                         \
-  case J_:                                                                                     \
-    hipLaunchKernelGGL(k_router_select<J_>, dim3((T + 3) / 4), dim3(256), 0, st, logits, bias, \
-                       idx, gate, counts, T, d.E, d.G, d.M, d.K);                              \
+  // the group lists have exactly J entries (J <= 8); at most 16 workgroups per CU, each
+  // then looping over its tokens, so the per-workgroup count histograms stay few
+  const int sel_wg = std::min((T + 3) / 4, 16 * device_cu_count());
+#define MOE_SELECT(J_)                                                                  \
+  case J_:                                                                              \
+    hipLaunchKernelGGL(k_router_select<J_>, dim3(sel_wg), dim3(256), 0, st, logits, bias, \
+                       idx, gate, counts, T, d.E, d.G, d.M, d.K);                       \
     break;
   switch (d.J) {
     MOE_SELECT(1) MOE_SELECT(2) MOE_SELECT(3) MOE_SELECT(4)

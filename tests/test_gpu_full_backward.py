@@ -1,6 +1,8 @@
 """GPU parity of the layer backward at the full DeepSeek-V3 layer shape (hidden 7168,
 256 routed experts + 1 shared, top-8 of 8 groups with at most 4 per token, SwiGLU width
-2048, bf16), in the dispatch form the benchmark times.
+2048, bf16), in the dispatch form the benchmark times; also at the decode size (T=128,
+most experts with a few rows or none) and on the skewed T=8192 batch (the most loaded
+experts span many row tiles).
 
 The oracle cannot run the whole backward at this size, so it computes what is local:
   * every gradient of a sampled token -- dgate, dz, the rows of dY and [da|du] that
@@ -46,7 +48,8 @@ def rows_of(layer, name, rows):
     return np_(getattr(layer, name)[torch.from_numpy(np.asarray(rows, np.int64)).cuda()])
 
 
-@pytest.mark.parametrize("name,n_tok,gather", [("v3-bf16", 6, True), ("v3-decode", 6, False)])
+@pytest.mark.parametrize("name,n_tok,gather", [("v3-bf16", 6, True), ("v3-decode", 6, False),
+                                               ("v3-skew-loop", 4, True)])
 def test_full_shape_backward(name, n_tok, gather):
     from mixture_experts_layer_added_amd.layer import MoELayer
     w = workloads.get(name)

@@ -50,8 +50,10 @@ def kernel_source_sha(expert, train=False):
     csrc = os.path.join(ROOT, "mixture_experts_layer_added_amd", "csrc")
     if train:
         files = ["gemm_bwd.hip", "common.h"]
+    elif expert == "e4m3":
+        files = ["gemm_fp8.hip", "common.h"]
     else:
-        files = ["gemm_fp8.hip" if expert == "e4m3" else "gemm.hip", "common.h"]
+        files = ["gemm.hip", "gemm_dense.hip", "common.h"]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
@@ -281,8 +283,9 @@ def main():
                     "traffic": None}
     else:
         up_gbs = gbs(up_bytes, avg_ms["ffn_up"])
-        roofline = {"kernel": "k_gemm_bf16<true> (gate/up grouped GEMM + SwiGLU)"
-                    if w.expert == "bf16" else f"gate/up grouped GEMM ({w.expert})",
+        roofline = {"kernel": "gate/up GEMM + SwiGLU call: k_gemm_bf16<true> (routed experts, "
+                              "grouped) + k_gemm_dense_swiglu_bf16 (the shared expert, when T >= "
+                              "2048)" if w.expert == "bf16" else f"gate/up grouped GEMM ({w.expert})",
                     "bound": "hbm", "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(up_gbs / HBM_PEAK_GBS, 4),
                     "bytes_per_launch": up_bytes, "ms_per_launch": round(avg_ms["ffn_up"], 4),

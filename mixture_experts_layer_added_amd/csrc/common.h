@@ -167,6 +167,14 @@ hipError_t launch_ffn_up(const Dims& d, const void* xs, const float* xs_scale,
 hipError_t launch_ffn_down(const Dims& d, const void* h, const float* h_scale,
                            const int32_t* offsets, const void* w2, const float* w2_scale, void* ys,
                            hipStream_t st);
+// The shared expert's gate/up GEMM + SwiGLU as a dense bf16 launch (gemm_dense.hip),
+// used when it has at least kDenseSharedMinRows rows (T); the grouped gate/up launch
+// then covers the routed experts only.  x [M, Kd] in token order, w13 [2*half, Kd]
+// (gate rows, then up rows), h [M, half], au [M, 2*half] optional.
+constexpr int64_t kDenseSharedMinRows = 2048;
+bool dense_shared(const Dims& d);
+hipError_t launch_dense_swiglu_bf16(const uint16_t* x, const uint16_t* w13, uint16_t* h,
+                                    uint16_t* au, int M, int Kd, int half, hipStream_t st);
 hipError_t launch_fp8_up(const Dims& d, const void* xs, const float* xs_scale,
                          const int32_t* offsets, const int32_t* gather, const void* w13,
                          const float* w13_scale, void* h, float* h_scale, hipStream_t st);

@@ -361,10 +361,21 @@ hipError_t launch_ffn_up(const Dims& d, const void* xs, const float* xs_scale,
     return hipGetLastError();
   }
   if (d.expert == MOE_BF16) {
+    int ng = NG;
+    if (dense_shared(d)) {  // the shared expert's rows T*K .. T*K+T-1, token order
+      ng = d.E;
+      const int64_t r0 = d.T * d.K;
+      const uint16_t* xa = static_cast<const uint16_t*>(xs) + (gather ? 0 : r0 * d.H);
+      uint16_t* aua = au ? static_cast<uint16_t*>(au) + r0 * 2 * d.I : nullptr;
+      const hipError_t e = launch_dense_swiglu_bf16(
+          xa, static_cast<const uint16_t*>(w13) + (int64_t)d.E * 2 * d.I * d.H,
+          static_cast<uint16_t*>(h) + r0 * d.I, aua, (int)d.T, d.H, d.I, st);
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(k_gemm_bf16<true>, dim3(persistent_grid(cus, 1)), dim3(512), 0, st,
                        static_cast<const uint16_t*>(xs), static_cast<const uint16_t*>(w13),
                        static_cast<uint16_t*>(h), offsets, gather, static_cast<uint16_t*>(au),
-                       (int)d.T, NG, d.H, 2 * d.I, d.I, d.I);
+                       (int)d.T, ng, d.H, 2 * d.I, d.I, d.I);
     return hipGetLastError();
   }
   return launch_fp8_up(d, xs, xs_scale, offsets, gather, w13, w13_scale, h, h_scale, st);

@@ -179,15 +179,18 @@ __global__ __launch_bounds__(256) void k_router_wgrad(const T* __restrict__ x,
   store8(dw + (int64_t)e * H + c, acc);
 }
 
-// Input gradient: one workgroup per (token, 2048-column slice).
+// Input gradient: one workgroup of 128 threads per (token, 1024-column slice), in a
+// linear token-major grid (the slices of one token are neighbours, so the pieces of each
+// row are read together).  dx = the router's part + the token's rows in rank order.
 template <typename T>
-__global__ __launch_bounds__(256) void k_unpermute_sum(const T* __restrict__ dxs,
+__global__ __launch_bounds__(128) void k_unpermute_sum(const T* __restrict__ dxs,
                                                        const int32_t* __restrict__ inv_perm,
                                                        const float* __restrict__ dxr,
                                                        T* __restrict__ dx, int Tn, int H, int K,
                                                        int S) {
-  const int t = blockIdx.x;
-  const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
+  const int nblk = (H / 8 + 127) / 128;
+  const int t = blockIdx.x / nblk;
+  const int c = ((blockIdx.x % nblk) * 128 + threadIdx.x) * 8;
   if (c >= H) return;
   float acc[8];
   if (dxr) {
@@ -253,13 +256,13 @@ hipError_t launch_router_bwd(const Dims& d, const void* x, const float* w, const
 hipError_t launch_unpermute_sum(const Dims& d, const void* dxs, const int32_t* inv_perm,
                                 const float* dxr, void* dx, hipStream_t st) {
   const int T = static_cast<int>(d.T);
-  const dim3 g(T, (d.H + 2047) / 2048);
+  const dim3 g(T * ((d.H / 8 + 127) / 128));
   if (d.act == MOE_BF16)
-    hipLaunchKernelGGL(k_unpermute_sum<uint16_t>, g, dim3(256), 0, st,
+    hipLaunchKernelGGL(k_unpermute_sum<uint16_t>, g, dim3(128), 0, st,
                        static_cast<const uint16_t*>(dxs), inv_perm, dxr,
                        static_cast<uint16_t*>(dx), T, d.H, d.K, d.S);
   else
-    hipLaunchKernelGGL(k_unpermute_sum<float>, g, dim3(256), 0, st,
+    hipLaunchKernelGGL(k_unpermute_sum<float>, g, dim3(128), 0, st,
                        static_cast<const float*>(dxs), inv_perm, dxr, static_cast<float*>(dx),
                        T, d.H, d.K, d.S);
   return hipGetLastError();

@@ -44,15 +44,19 @@ __device__ __forceinline__ void widen(const uint4& u, float* v) {
 // One workgroup of 128 threads per (token, 128 chunks of 16 bytes); each thread owns 16
 // bytes of the row.  All K+1 rows are loaded before the first multiply-add (the loads are
 // independent, so they are all in flight together), then summed in rank order.  Y is
-// read once and y is not read again here: both go non-temporal.
+// read once and y is not read again here: both go non-temporal.  The grid is linear and
+// token-major (the workgroups of one token are neighbours), so the pieces of each 14 KB
+// row are read at about the same time: DRAM pages are opened once per row, not once per
+// piece (0.110 -> 0.095 ms at the V3 shape).
 template <typename T>
 __global__ __launch_bounds__(128) void k_combine(const T* __restrict__ ys,
                                                  const int32_t* __restrict__ inv_perm,
                                                  const float* __restrict__ gate, T* __restrict__ y,
                                                  int Tn, int H, int K, int S) {
   constexpr int V = 16 / sizeof(T);
-  const int t = blockIdx.x;
-  const int c = blockIdx.y * 128 + threadIdx.x;
+  const int nblk = (H / V + 127) / 128;
+  const int t = blockIdx.x / nblk;
+  const int c = (blockIdx.x % nblk) * 128 + threadIdx.x;
   if (c * V >= H) return;
   uint4 u[kMaxK];
   int row[kMaxK];
@@ -157,12 +161,12 @@ hipError_t launch_combine(const Dims& d, const void* ys, const int32_t* inv_perm
                           const float* gate, void* y, hipStream_t st) {
   const int T = static_cast<int>(d.T);
   if (d.act == MOE_BF16) {
-    dim3 grid(T, (d.H / 8 + 127) / 128);
+    dim3 grid(T * ((d.H / 8 + 127) / 128));
     hipLaunchKernelGGL(k_combine<uint16_t>, grid, dim3(128), 0, st,
                        static_cast<const uint16_t*>(ys), inv_perm, gate,
                        static_cast<uint16_t*>(y), T, d.H, d.K, d.S);
   } else {
-    dim3 grid(T, (d.H / 4 + 127) / 128);
+    dim3 grid(T * ((d.H / 4 + 127) / 128));
     hipLaunchKernelGGL(k_combine<float>, grid, dim3(128), 0, st, static_cast<const float*>(ys),
                        inv_perm, gate, static_cast<float*>(y), T, d.H, d.K, d.S);
   }

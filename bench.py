@@ -51,7 +51,7 @@ def kernel_source_sha(expert, train=False):
     if train:
         files = ["gemm_bwd.hip", "common.h"]
     elif expert == "e4m3":
-        files = ["gemm_fp8.hip", "common.h"]
+        files = ["gemm_fp8.hip", "gemm_dense.hip", "common.h"]
     else:
         files = ["gemm.hip", "gemm_dense.hip", "common.h"]
     h = hashlib.sha256()
@@ -285,7 +285,9 @@ def main():
         up_gbs = gbs(up_bytes, avg_ms["ffn_up"])
         roofline = {"kernel": "gate/up GEMM + SwiGLU call: k_gemm_bf16<true> (routed experts, "
                               "grouped) + k_gemm_dense_swiglu_bf16 (the shared expert, when T >= "
-                              "2048)" if w.expert == "bf16" else f"gate/up grouped GEMM ({w.expert})",
+                              "2048)" if w.expert == "bf16" else
+                    "gate/up GEMM + SwiGLU call (e4m3): k_gemm_fp8<true> (routed experts, grouped) "
+                    "+ k_gemm_dense_swiglu_fp8 (the shared expert, when T >= 2048)",
                     "bound": "hbm", "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(up_gbs / HBM_PEAK_GBS, 4),
                     "bytes_per_launch": up_bytes, "ms_per_launch": round(avg_ms["ffn_up"], 4),

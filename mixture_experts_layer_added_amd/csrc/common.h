@@ -167,9 +167,9 @@ hipError_t launch_ffn_up(const Dims& d, const void* xs, const float* xs_scale,
 hipError_t launch_ffn_down(const Dims& d, const void* h, const float* h_scale,
                            const int32_t* offsets, const void* w2, const float* w2_scale, void* ys,
                            hipStream_t st);
-// The shared expert's gate/up GEMM + SwiGLU as a dense bf16 launch (gemm_dense.hip),
-// used when it has at least kDenseSharedMinRows rows (T); the grouped gate/up launch
-// then covers the routed experts only.  x [M, Kd] in token order, w13 [2*half, Kd]
+// The shared expert's gate/up GEMM + SwiGLU as a dense launch (bf16: gemm_dense.hip,
+// FP8: gemm_fp8.hip), used when it has at least kDenseSharedMinRows rows (T); the
+// grouped gate/up launch then covers the routed experts only.  x [M, Kd] in token order, w13 [2*half, Kd]
 // (gate rows, then up rows), h [M, half], au [M, 2*half] optional.
 constexpr int64_t kDenseSharedMinRows = 2048;
 bool dense_shared(const Dims& d);

@@ -177,7 +177,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dense_swiglu_bf16(
 }  // namespace
 
 bool dense_shared(const Dims& d) {
-  return d.S == 1 && d.expert == MOE_BF16 && d.T >= kDenseSharedMinRows;
+  return d.S == 1 && (d.expert == MOE_BF16 || d.expert == MOE_FP8_E4M3) &&
+         d.T >= kDenseSharedMinRows;
 }
 
 hipError_t launch_dense_swiglu_bf16(const uint16_t* x, const uint16_t* w13, uint16_t* h,

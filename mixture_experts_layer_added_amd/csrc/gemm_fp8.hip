@@ -270,6 +270,178 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(
   }
 }
 
+// The shared expert's gate/up as a dense FP8 GEMM (at T >= kDenseSharedMinRows; the
+// grouped launch then covers the routed experts).  Its full-height tiles in the grouped
+// launch get one 64 KiB step in flight and stall on the L2; here tiles are 128 rows x
+// 256 weight rows, so a step (16 KiB of codes + 32 KiB of weights + 512 B of scales)
+// fits three times in LDS, two in flight, and all eight waves multiply: wave (wm, wn)
+// owns rows 32wm .. +31 and the sub-tiles 4wn .. 4wn+3 of [g0 u0 g1 u1 g2 u2 g3 u3]
+// (32 columns each), i.e. h columns 64wn .. +63 of the tile's 128.  The per-block
+// promotion acc += partial * (s_a * s_w) is the grouped kernel's; an h row's 128-column
+// quantisation tile spans the two waves wn = 0, 1, so its amax is combined through LDS.
+// Tiles in bands of eight row tiles, column-major inside a band, one contiguous range
+// of that order per XCD.
+constexpr int QBM = 128, QBand = 8;
+constexpr int kQA = QBM * FBK;        // A stage: 16 KiB
+constexpr int kQStage = kQA + kFB;    // 48 KiB
+constexpr int kQRing = 3;
+
+__global__ __launch_bounds__(512, 1) void k_gemm_dense_swiglu_fp8(
+    const uint8_t* __restrict__ A, const float* __restrict__ A_scale,
+    const uint8_t* __restrict__ B, const float* __restrict__ B_scale, uint8_t* __restrict__ h,
+    float* __restrict__ h_scale, int M, int Kd, int half, int mt, int nt) {
+  __shared__ __attribute__((aligned(1024))) char smem[kQRing * kQStage];
+  __shared__ __attribute__((aligned(16))) float s_sa[kQRing][QBM];
+  __shared__ float s_amax[2][QBM];
+  const int total = mt * nt;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (tile >= total) return;
+  const int band = tile / (QBand * nt), within = tile % (QBand * nt);
+  const int rb = min(QBand, mt - band * QBand);
+  const int n_idx = within / rb, m_idx = band * QBand + within % rb;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv >> 1, wn = wv & 1;
+  const int nk = Kd / FBK;      // k steps = scale blocks along k
+  const int m0 = m_idx * QBM;
+  const int m_rows = min(QBM, M - m0);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
+  const uint32_t lds_sa = __builtin_amdgcn_readfirstlane(lds_offset(&s_sa[0][0]));
+  // loader: instruction i of wave wv fills rows 64i + 8wv .. +7 of an operand stage;
+  // lane l writes row 64i + 8wv + (l>>3), slot l&7 (chunk (l&7) ^ ((row>>1)&7))
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ ((4 * (wv & 1) + (lane >> 4)) & 7);
+  const int kq = lane >> 5;
+  // codes and scales of rows past M read as zeros (range check)
+  const i32x4 arsrc = buffer_rsrc(A + (int64_t)m0 * Kd, (uint32_t)m_rows * Kd);
+  const i32x4 brsrc = buffer_rsrc(B, (uint32_t)(2 * half) * Kd);
+  const i32x4 srsrc = buffer_rsrc(A_scale + (int64_t)m0 * nk, (uint32_t)m_rows * nk * 4);
+  uint32_t aoff[2], boff[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) aoff[i] = (uint32_t)((64 * i + 8 * wv + lrow) * Kd + lchunk * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 64 * i + 8 * wv + lrow;
+    const int br = r < 128 ? n_idx * 128 + r : half + n_idx * 128 + (r - 128);
+    boff[i] = (uint32_t)(br * Kd + lchunk * 16);
+  }
+  const bool ld_sa = wv < 2;  // waves 0, 1 bring 64 activation scales each
+  const uint32_t soff = (uint32_t)((64 * wv + lane) * nk) * 4;
+  const uint32_t ldsw = lds0 + 8 * wv * FBK;
+  const uint32_t ldss = lds_sa + 64 * wv * 4;
+  const int per_stage = 6 + (ld_sa ? 1 : 0);
+  const float* bsc0 = B_scale + (int64_t)n_idx * nk;                  // gate block row
+  const float* bsc1 = B_scale + (int64_t)(half / 128 + n_idx) * nk;   // up block row
+
+#define QSTAGE_LOAD(kt, st)                                                           \
+  {                                                                                   \
+    const uint32_t sa_ = ldsw + (st) * kQStage;                                       \
+    const uint32_t ko_ = (uint32_t)(kt) * FBK;                                        \
+    load16_to_lds(arsrc, sa_, aoff[0] + ko_);                                         \
+    load16_to_lds(arsrc, sa_ + 64 * FBK, aoff[1] + ko_);                              \
+    load16_to_lds(brsrc, sa_ + kQA, boff[0] + ko_);                                   \
+    load16_to_lds(brsrc, sa_ + kQA + 64 * FBK, boff[1] + ko_);                        \
+    load16_to_lds(brsrc, sa_ + kQA + 128 * FBK, boff[2] + ko_);                       \
+    load16_to_lds(brsrc, sa_ + kQA + 192 * FBK, boff[3] + ko_);                       \
+    if (ld_sa) load4_to_lds(srsrc, ldss + (st) * (QBM * 4), soff + (uint32_t)(kt) * 4); \
+  }
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[n][i] = 0.0f;
+  const int arow = 32 * wm + (lane & 31);
+
+  QSTAGE_LOAD(0, 0)
+  if (nk > 1) QSTAGE_LOAD(1, 1)
+  int st = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const float sw0 = bsc0[kt];
+    const float sw1 = bsc1[kt];
+    wait_vmcnt(min(kQRing - 2, nk - 1 - kt) * per_stage);
+    __syncthreads();
+    if (kt + kQRing - 1 < nk) {
+      int sn = st + kQRing - 1;
+      if (sn >= kQRing) sn -= kQRing;
+      QSTAGE_LOAD(kt + kQRing - 1, sn)
+    }
+    const char* as = smem + st * kQStage;
+    const char* bs = as + kQA;
+    // A fragments of both 64-deep halves: chunks 2*kq, 2*kq+1 and 4 + the same
+    const i32x8 a0 = frag32(as + fswz(arow, 2 * kq), as + fswz(arow, 2 * kq + 1));
+    const i32x8 a1 = frag32(as + fswz(arow, 4 + 2 * kq), as + fswz(arow, 5 + 2 * kq));
+    float sa[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(&s_sa[st][32 * wm + 8 * q + 4 * kq]);
+      sa[4 * q + 0] = v.x; sa[4 * q + 1] = v.y; sa[4 * q + 2] = v.z; sa[4 * q + 3] = v.w;
+    }
+#pragma unroll
+    for (int n = 0; n < 4; n += 2) {
+      f32x16 t[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int nn = 4 * wn + n + u;
+        const int brow = (nn & 1) * 128 + 32 * (nn >> 1) + (lane & 31);
+        const i32x8 b0 = frag32(bs + fswz(brow, 2 * kq), bs + fswz(brow, 2 * kq + 1));
+        f32x16 z;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+        t[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, z, 0, 0, 0, 127, 0, 127);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int nn = 4 * wn + n + u;
+        const int brow = (nn & 1) * 128 + 32 * (nn >> 1) + (lane & 31);
+        const i32x8 b1 = frag32(bs + fswz(brow, 4 + 2 * kq), bs + fswz(brow, 5 + 2 * kq));
+        t[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, t[u], 0, 0, 0, 127, 0, 127);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float sw = (u & 1) ? sw1 : sw0;  // sub-tile parity: gate even, up odd
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          acc[n + u][i] = __builtin_fmaf(t[u][i], sa[i] * sw, acc[n + u][i]);
+      }
+    }
+    if (++st == kQRing) st = 0;
+  }
+#undef QSTAGE_LOAD
+
+  // h = silu(gate) * up; this wave holds 64 of the row's 128 quantisation columns
+  float hv[2][16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float m = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      hv[t][i] = silu(acc[2 * t][i]) * acc[2 * t + 1][i];
+      m = __builtin_fmaxf(m, __builtin_fabsf(hv[t][i]));
+    }
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+    if ((lane & 31) == 0) s_amax[wn][32 * wm + 8 * (i >> 2) + 4 * kq + (i & 3)] = m;
+  }
+  __syncthreads();
+  const int ncb = half / 128;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 32 * wm + 8 * (i >> 2) + 4 * kq + (i & 3);
+    if (r >= m_rows) continue;
+    const float m = __builtin_fmaxf(s_amax[0][r], s_amax[1][r]);
+    const float sc = m > 0.0f ? m / 448.0f : 1.0f;
+    uint8_t* hp = h + (int64_t)(m0 + r) * half + n_idx * 128 + 64 * wn + (lane & 31);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      __builtin_nontemporal_store(static_cast<uint8_t>(f32_to_e4m3_bits(hv[t][i] / sc)),
+                                  hp + 32 * t);
+    if (wn == 0 && (lane & 31) == 0) h_scale[(int64_t)(m0 + r) * ncb + n_idx] = sc;
+  }
+}
+
 int fp8_grid(int cus) {
   const int p = (cus / kXcds) * kXcds;
   return p < kXcds ? kXcds : p;
@@ -280,9 +452,26 @@ int fp8_grid(int cus) {
 hipError_t launch_fp8_up(const Dims& d, const void* xs, const float* xs_scale,
                          const int32_t* offsets, const int32_t* gather, const void* w13,
                          const float* w13_scale, void* h, float* h_scale, hipStream_t st) {
+  int ng = d.E + d.S;
+  if (dense_shared(d)) {  // the shared expert's rows T*K .. T*K+T-1, token order
+    ng = d.E;
+    const int64_t r0 = d.T * d.K;
+    const int nkb = d.H / 128;
+    const uint8_t* xa = static_cast<const uint8_t*>(xs) + (gather ? 0 : r0 * d.H);
+    const float* xsa = xs_scale + (gather ? 0 : r0 * nkb);
+    const int mt = (int)((d.T + QBM - 1) / QBM), nt = d.I / 128;
+    const int per = (mt * nt + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL(k_gemm_dense_swiglu_fp8, dim3(per * kXcds), dim3(512), 0, st, xa, xsa,
+                       static_cast<const uint8_t*>(w13) + (int64_t)d.E * 2 * d.I * d.H,
+                       w13_scale + (int64_t)d.E * (2 * d.I / 128) * nkb,
+                       static_cast<uint8_t*>(h) + r0 * d.I, h_scale + r0 * (d.I / 128),
+                       (int)d.T, d.H, d.I, mt, nt);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((k_gemm_fp8<true>), dim3(fp8_grid(device_cu_count())), dim3(512), 0, st,
                      static_cast<const uint8_t*>(xs), xs_scale, static_cast<const uint8_t*>(w13),
-                     w13_scale, h, h_scale, offsets, gather, (int)d.T, d.E + d.S, d.H, 2 * d.I,
+                     w13_scale, h, h_scale, offsets, gather, (int)d.T, ng, d.H, 2 * d.I,
                      d.I, d.I);
   return hipGetLastError();
 }

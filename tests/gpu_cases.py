@@ -21,9 +21,10 @@ SMALL_CASES = {
     "allgroups-bf16": ("v3-bf16", dict(T=200, H=256, E=64, G=8, M=8, K=8, J=3, I=128)),
     "maxE-bf16": ("v3-bf16", dict(T=130, H=128, E=512, G=64, M=4, K=16, J=8, I=128)),
     # T >= 2048 with a shared expert: its gate/up GEMM runs as a dense launch (ragged
-    # last row tile)
+    # last row tile; dense-fp8 below is the FP8 counterpart)
     "dense-bf16": ("v3-bf16", dict(T=2100, H=384, E=16, G=4, M=2, K=4, J=2, I=384)),
     "ragged-fp8": ("v3-fp8", dict(T=700, H=384, E=16, G=4, M=2, K=4, J=2, I=256)),
+    "dense-fp8": ("v3-fp8", dict(T=2100, H=384, E=16, G=4, M=2, K=4, J=2, I=256)),
     "v3route-fp8": ("v3-fp8", dict(T=300, H=256, I=256)),
 }
 

@@ -181,7 +181,8 @@ __global__ __launch_bounds__(256) void k_router_wgrad(const T* __restrict__ x,
 
 // Input gradient: one workgroup of 128 threads per (token, 1024-column slice), in a
 // linear token-major grid (the slices of one token are neighbours, so the pieces of each
-// row are read together).  dx = the router's part + the token's rows in rank order.
+// row are read together; the grid strides over (token, slice) items).  dx = the
+// router's part + the token's rows in rank order.
 template <typename T>
 __global__ __launch_bounds__(128) void k_unpermute_sum(const T* __restrict__ dxs,
                                                        const int32_t* __restrict__ inv_perm,
@@ -189,31 +190,34 @@ __global__ __launch_bounds__(128) void k_unpermute_sum(const T* __restrict__ dxs
                                                        T* __restrict__ dx, int Tn, int H, int K,
                                                        int S) {
   const int nblk = (H / 8 + 127) / 128;
-  const int t = blockIdx.x / nblk;
-  const int c = ((blockIdx.x % nblk) * 128 + threadIdx.x) * 8;
-  if (c >= H) return;
-  float acc[8];
-  if (dxr) {
-    load8(dxr + (int64_t)t * H + c, acc);
-  } else {
+  const int64_t work = (int64_t)Tn * nblk;
+  for (int64_t b = blockIdx.x; b < work; b += gridDim.x) {
+    const int t = (int)(b / nblk);
+    const int c = ((int)(b % nblk) * 128 + threadIdx.x) * 8;
+    if (c >= H) continue;
+    float acc[8];
+    if (dxr) {
+      load8(dxr + (int64_t)t * H + c, acc);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  }
-  for (int k = 0; k < K; ++k) {
-    const int row = inv_perm[(int64_t)t * K + k];
-    if (row < 0) continue;
-    float v[8];
-    load8(dxs + (int64_t)row * H + c, v);
+      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    }
+    for (int k = 0; k < K; ++k) {
+      const int row = inv_perm[(int64_t)t * K + k];
+      if (row < 0) continue;
+      float v[8];
+      load8(dxs + (int64_t)row * H + c, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += v[i];
-  }
-  if (S) {
-    float v[8];
-    load8(dxs + ((int64_t)Tn * K + t) * H + c, v);
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    if (S) {
+      float v[8];
+      load8(dxs + ((int64_t)Tn * K + t) * H + c, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    store8(dx + (int64_t)t * H + c, acc);
   }
-  store8(dx + (int64_t)t * H + c, acc);
 }
 
 }  // namespace
@@ -256,7 +260,7 @@ hipError_t launch_router_bwd(const Dims& d, const void* x, const float* w, const
 hipError_t launch_unpermute_sum(const Dims& d, const void* dxs, const int32_t* inv_perm,
                                 const float* dxr, void* dx, hipStream_t st) {
   const int T = static_cast<int>(d.T);
-  const dim3 g(T * ((d.H / 8 + 127) / 128));
+  const dim3 g((unsigned)std::min<int64_t>((int64_t)T * ((d.H / 8 + 127) / 128), 1 << 20));
   if (d.act == MOE_BF16)
     hipLaunchKernelGGL(k_unpermute_sum<uint16_t>, g, dim3(128), 0, st,
                        static_cast<const uint16_t*>(dxs), inv_perm, dxr,

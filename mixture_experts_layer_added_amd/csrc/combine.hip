@@ -47,7 +47,7 @@ __device__ __forceinline__ void widen(const uint4& u, float* v) {
 // read once and y is not read again here: both go non-temporal.  The grid is linear and
 // token-major (the workgroups of one token are neighbours), so the pieces of each 14 KB
 // row are read at about the same time: DRAM pages are opened once per row, not once per
-// piece (0.110 -> 0.095 ms at the V3 shape).
+// piece (0.110 -> 0.095 ms at the V3 shape).  The grid strides over (token, slice) items.
 template <typename T>
 __global__ __launch_bounds__(128) void k_combine(const T* __restrict__ ys,
                                                  const int32_t* __restrict__ inv_perm,
@@ -55,50 +55,53 @@ __global__ __launch_bounds__(128) void k_combine(const T* __restrict__ ys,
                                                  int Tn, int H, int K, int S) {
   constexpr int V = 16 / sizeof(T);
   const int nblk = (H / V + 127) / 128;
-  const int t = blockIdx.x / nblk;
-  const int c = (blockIdx.x % nblk) * 128 + threadIdx.x;
-  if (c * V >= H) return;
-  uint4 u[kMaxK];
-  int row[kMaxK];
+  const int64_t work = (int64_t)Tn * nblk;
+  for (int64_t b = blockIdx.x; b < work; b += gridDim.x) {
+    const int t = (int)(b / nblk);
+    const int c = (int)(b % nblk) * 128 + threadIdx.x;
+    if (c * V >= H) continue;
+    uint4 u[kMaxK];
+    int row[kMaxK];
 #pragma unroll
-  for (int k = 0; k < kMaxK; ++k) {
-    row[k] = k < K ? inv_perm[(int64_t)t * K + k] : -1;
-    if (row[k] >= 0)
-      u[k] = ld_nt(ys + (int64_t)row[k] * H + c * V);
+    for (int k = 0; k < kMaxK; ++k) {
+      row[k] = k < K ? inv_perm[(int64_t)t * K + k] : -1;
+      if (row[k] >= 0)
+        u[k] = ld_nt(ys + (int64_t)row[k] * H + c * V);
+    }
+    uint4 us = make_uint4(0, 0, 0, 0);
+    if (S) us = ld_nt(ys + ((int64_t)Tn * K + t) * H + c * V);
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+      if (row[k] < 0) continue;
+      const float g = gate[(int64_t)t * K + k];
+      float v[V];
+      widen<T>(u[k], v);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = __builtin_fmaf(g, v[i], acc[i]);
+    }
+    if (S) {
+      float v[V];
+      widen<T>(us, v);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = v[i] + acc[i];
+    }
+    uint4 o;
+    if constexpr (sizeof(T) == 2) {
+      o.x = f32_to_bf16_bits(acc[0]) | (uint32_t)f32_to_bf16_bits(acc[1]) << 16;
+      o.y = f32_to_bf16_bits(acc[2]) | (uint32_t)f32_to_bf16_bits(acc[3]) << 16;
+      o.z = f32_to_bf16_bits(acc[4]) | (uint32_t)f32_to_bf16_bits(acc[5]) << 16;
+      o.w = f32_to_bf16_bits(acc[6]) | (uint32_t)f32_to_bf16_bits(acc[7]) << 16;
+    } else {
+      o.x = __float_as_uint(acc[0]);
+      o.y = __float_as_uint(acc[1]);
+      o.z = __float_as_uint(acc[2]);
+      o.w = __float_as_uint(acc[3]);
+    }
+    st_nt(y + (int64_t)t * H + c * V, o);
   }
-  uint4 us = make_uint4(0, 0, 0, 0);
-  if (S) us = ld_nt(ys + ((int64_t)Tn * K + t) * H + c * V);
-  float acc[V];
-#pragma unroll
-  for (int i = 0; i < V; ++i) acc[i] = 0.0f;
-#pragma unroll
-  for (int k = 0; k < kMaxK; ++k) {
-    if (row[k] < 0) continue;
-    const float g = gate[(int64_t)t * K + k];
-    float v[V];
-    widen<T>(u[k], v);
-#pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = __builtin_fmaf(g, v[i], acc[i]);
-  }
-  if (S) {
-    float v[V];
-    widen<T>(us, v);
-#pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = v[i] + acc[i];
-  }
-  uint4 o;
-  if constexpr (sizeof(T) == 2) {
-    o.x = f32_to_bf16_bits(acc[0]) | (uint32_t)f32_to_bf16_bits(acc[1]) << 16;
-    o.y = f32_to_bf16_bits(acc[2]) | (uint32_t)f32_to_bf16_bits(acc[3]) << 16;
-    o.z = f32_to_bf16_bits(acc[4]) | (uint32_t)f32_to_bf16_bits(acc[5]) << 16;
-    o.w = f32_to_bf16_bits(acc[6]) | (uint32_t)f32_to_bf16_bits(acc[7]) << 16;
-  } else {
-    o.x = __float_as_uint(acc[0]);
-    o.y = __float_as_uint(acc[1]);
-    o.z = __float_as_uint(acc[2]);
-    o.w = __float_as_uint(acc[3]);
-  }
-  st_nt(y + (int64_t)t * H + c * V, o);
 }
 
 __global__ void k_bias_update(const int32_t* __restrict__ counts, float* __restrict__ bias,
@@ -161,12 +164,12 @@ hipError_t launch_combine(const Dims& d, const void* ys, const int32_t* inv_perm
                           const float* gate, void* y, hipStream_t st) {
   const int T = static_cast<int>(d.T);
   if (d.act == MOE_BF16) {
-    dim3 grid(T * ((d.H / 8 + 127) / 128));
+    dim3 grid((unsigned)std::min<int64_t>((int64_t)T * ((d.H / 8 + 127) / 128), 1 << 20));
     hipLaunchKernelGGL(k_combine<uint16_t>, grid, dim3(128), 0, st,
                        static_cast<const uint16_t*>(ys), inv_perm, gate,
                        static_cast<uint16_t*>(y), T, d.H, d.K, d.S);
   } else {
-    dim3 grid(T * ((d.H / 4 + 127) / 128));
+    dim3 grid((unsigned)std::min<int64_t>((int64_t)T * ((d.H / 4 + 127) / 128), 1 << 20));
     hipLaunchKernelGGL(k_combine<float>, grid, dim3(128), 0, st, static_cast<const float*>(ys),
                        inv_perm, gate, static_cast<float*>(y), T, d.H, d.K, d.S);
   }

@@ -177,8 +177,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dense_swiglu_bf16(
 }  // namespace
 
 bool dense_shared(const Dims& d) {
+  // one workgroup per tile (tiles of at least 128 rows x 128 h columns): beyond 2^22
+  // tiles the dispatch would exceed 2^31 work-items, and the grouped launch (persistent)
+  // keeps the shared expert instead
+  const int64_t max_tiles = ((d.T + 127) / 128) * (int64_t)(d.I / 128);
   return d.S == 1 && (d.expert == MOE_BF16 || d.expert == MOE_FP8_E4M3) &&
-         d.T >= kDenseSharedMinRows;
+         d.T >= kDenseSharedMinRows && max_tiles <= ((int64_t)1 << 22);
 }
 
 hipError_t launch_dense_swiglu_bf16(const uint16_t* x, const uint16_t* w13, uint16_t* h,

@@ -21,15 +21,18 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Logits: lanes are tokens, experts are wave-uniform.  A workgroup takes 64 tokens x
-// 32 experts; its 8 waves share the tokens' hidden chunk (64 h at a time, in LDS as
-// fp32, one padded row per token) and each wave owns 4 experts, whose router-weight
+// 8*kRE experts; its 8 waves share the tokens' hidden chunk (64 h at a time, in LDS as
+// fp32, one padded row per token) and each wave owns kRE experts, whose router-weight
 // rows it reads with scalar loads, so each fused multiply-add takes its weight operand
 // from a scalar register and its x operand from the lane's own row.  Every
-// accumulator sees h in increasing order.
+// accumulator sees h in increasing order.  kRE = 4 when there are enough tokens to fill
+// the GPU (fewer weight loads per multiply-add); up to 3072 tokens kRE = 1, which gives
+// four times as many waves to hide the latency of the chunk loads (T=128: 0.22 ->
+// 0.10 ms, T=2048: 0.31 -> 0.26 ms; logits unchanged bit for bit).
 // ---------------------------------------------------------------------------
-constexpr int RT = 64, RE = 4, RWV = 8, RH = 64, RROW = RH + 4;
+constexpr int RT = 64, RWV = 8, RH = 64, RROW = RH + 4;
 
-template <typename XT>
+template <typename XT, int RE>
 __global__ __launch_bounds__(RWV * kWave) void k_router_logits(const XT* __restrict__ x,
                                                                const float* __restrict__ w,
                                                                float* __restrict__ z,
@@ -285,13 +288,24 @@ hipError_t launch_route(const Dims& d, const void* x, const float* w_router, con
                         int32_t* idx, float* gate, int32_t* counts, float* logits,
                         hipStream_t st) {
   const int T = static_cast<int>(d.T);
-  dim3 g1((T + RT - 1) / RT, (d.E + RE * RWV - 1) / (RE * RWV));
-  if (d.act == MOE_BF16)
-    hipLaunchKernelGGL(k_router_logits<uint16_t>, g1, dim3(RWV * kWave), 0, st,
-                       static_cast<const uint16_t*>(x), w_router, logits, counts, T, d.H, d.E);
-  else
-    hipLaunchKernelGGL(k_router_logits<float>, g1, dim3(RWV * kWave), 0, st,
-                       static_cast<const float*>(x), w_router, logits, counts, T, d.H, d.E);
+  const bool few = T <= 3072;
+  const int re = few ? 1 : 4;
+  dim3 g1((T + RT - 1) / RT, (d.E + re * RWV - 1) / (re * RWV));
+  if (d.act == MOE_BF16) {
+    if (few)
+      hipLaunchKernelGGL((k_router_logits<uint16_t, 1>), g1, dim3(RWV * kWave), 0, st,
+                         static_cast<const uint16_t*>(x), w_router, logits, counts, T, d.H, d.E);
+    else
+      hipLaunchKernelGGL((k_router_logits<uint16_t, 4>), g1, dim3(RWV * kWave), 0, st,
+                         static_cast<const uint16_t*>(x), w_router, logits, counts, T, d.H, d.E);
+  } else {
+    if (few)
+      hipLaunchKernelGGL((k_router_logits<float, 1>), g1, dim3(RWV * kWave), 0, st,
+                         static_cast<const float*>(x), w_router, logits, counts, T, d.H, d.E);
+    else
+      hipLaunchKernelGGL((k_router_logits<float, 4>), g1, dim3(RWV * kWave), 0, st,
+                         static_cast<const float*>(x), w_router, logits, counts, T, d.H, d.E);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the group lists have exactly J entries (J <= 8); at most 16 workgroups per CU, each

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kRowBytes = BK * 2;               // one row of one stage: a full 128-B line
 constexpr int kBStage = BN * kRowBytes;         // 32 KiB
-constexpr int kRing = 3 * (128 * kRowBytes + kBStage);  // 144 KiB
+constexpr int kRing = 3 * (144 * kRowBytes + kBStage);  // 150 KiB: 3 stages up to 144 A rows
 
 // byte offset of (row, 16-byte k-chunk c) inside an operand stage: rows of 128 B,
 // chunk slots xor-swizzled by (row >> 1) & 7 so 16 consecutive rows at one chunk hit
@@ -200,12 +200,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
     const int m_rows = min(BM, m_g - m0);
     const bool w_on = 64 * wm < m_rows && (kSwiglu || tl.n_idx * BN + 128 * wn < Nout);
     const bool w_sub1 = 64 * wm + 32 < m_rows;
-    // ring shape of this tile: A stage holds nA*64 rows; three stages when they fit
+    // ring shape of this tile: three stages when an A stage of the rows rounded up to 16
+    // fits three times (experts of up to 144 rows), else two stages of nA*64 rows.  A
+    // rows past the expert's end that are not loaded hold stale data: their products
+    // land in output rows that are not stored.
     const int nA = (m_rows + 63) >> 6;
-    const int sA = nA * 64 * kRowBytes;
+    const int rA16 = (m_rows + 15) & ~15;
+    const bool three = 3 * (rA16 * kRowBytes + kBStage) <= kRing;
+    const int rowsA = three ? rA16 : nA * 64;
+    const int sA = rowsA * kRowBytes;
     const int sStage = sA + kBStage;
-    const int nst = (3 * sStage <= kRing) ? 3 : 2;
-    const int per_stage = nA + 4;  // loads per thread per stage
+    const int nst = three ? 3 : 2;
+    // A load instructions of this wave (instruction i covers rows 64i + 8wv .. +7)
+    const int nAw = __builtin_amdgcn_readfirstlane((rowsA - 8 * wv + 63) >> 6);
+    const int per_stage = nAw + 4;  // loads per thread per stage
 
     // A rows past the expert's end and B rows past Nout read as zeros (range check)
     const i32x4 arsrc =
@@ -231,10 +239,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
   {                                                                                   \
     const uint32_t sa_ = ldsw + (st) * sStage;                                        \
     const uint32_t ko_ = (uint32_t)(kt) * kRowBytes;                                  \
-    load16_to_lds(arsrc, sa_, aoff[0] + ko_);                                           \
-    if (nA > 1) load16_to_lds(arsrc, sa_ + 64 * kRowBytes, aoff[1] + ko_);              \
-    if (nA > 2) load16_to_lds(arsrc, sa_ + 128 * kRowBytes, aoff[2] + ko_);             \
-    if (nA > 3) load16_to_lds(arsrc, sa_ + 192 * kRowBytes, aoff[3] + ko_);             \
+    if (nAw > 0) load16_to_lds(arsrc, sa_, aoff[0] + ko_);                              \
+    if (nAw > 1) load16_to_lds(arsrc, sa_ + 64 * kRowBytes, aoff[1] + ko_);             \
+    if (nAw > 2) load16_to_lds(arsrc, sa_ + 128 * kRowBytes, aoff[2] + ko_);            \
+    if (nAw > 3) load16_to_lds(arsrc, sa_ + 192 * kRowBytes, aoff[3] + ko_);            \
     load16_to_lds_nt(brsrc, sa_ + sA, boff[0] + ko_);                                      \
     load16_to_lds_nt(brsrc, sa_ + sA + 64 * kRowBytes, boff[1] + ko_);                     \
     load16_to_lds_nt(brsrc, sa_ + sA + 128 * kRowBytes, boff[2] + ko_);                    \

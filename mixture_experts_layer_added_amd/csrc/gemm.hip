@@ -131,9 +131,9 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
 // bit, no register staging).  Weight loads and output stores are non-temporal: a
 // weight tile is read only by the few workgroups working on it at the same moment and
 // outputs are not read again here, so the L2 is left to the activation rows that
-// every column tile of an expert re-reads.  The LDS ring is shaped per tile: the A stage holds
-// ceil(rows/64)*64 rows, and when a stage fits three times into 144 KiB (experts of
-// <= 128 rows) two steps are in flight while one is multiplied, else one.
+// every column tile of an expert re-reads.  The LDS ring is shaped per tile: experts of
+// up to 144 rows get three stages (A part = rows rounded up to 16), so two steps are in
+// flight while one is multiplied; larger ones two stages of ceil(rows/64)*64 A rows.
 // Activation rows past the expert's end are read through a buffer descriptor sized
 // to the expert's rows, so they arrive as zeros with no memory traffic.
 // One workgroup of 8 waves per CU: wave w owns rows 64*(w/2) .. +63 and columns

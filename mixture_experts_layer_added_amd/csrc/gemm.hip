@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
 // weight tile is read only by the few workgroups working on it at the same moment and
 // outputs are not read again here, so the L2 is left to the activation rows that
 // every column tile of an expert re-reads.  The LDS ring is shaped per tile: experts of
-// up to 144 rows get three stages (A part = rows rounded up to 16), so two steps are in
+// up to 160 rows get three stages (A part = rows rounded up to 16), so two steps are in
 // flight while one is multiplied; larger ones two stages of ceil(rows/64)*64 A rows.
 // Activation rows past the expert's end are read through a buffer descriptor sized
 // to the expert's rows, so they arrive as zeros with no memory traffic.
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kRowBytes = BK * 2;               // one row of one stage: a full 128-B line
 constexpr int kBStage = BN * kRowBytes;         // 32 KiB
-constexpr int kRing = 3 * (144 * kRowBytes + kBStage);  // 150 KiB: 3 stages up to 144 A rows
+constexpr int kRing = 3 * (160 * kRowBytes + kBStage);  // 156 KiB: 3 stages up to 160 A rows
 
 // byte offset of (row, 16-byte k-chunk c) inside an operand stage: rows of 128 B,
 // chunk slots xor-swizzled by (row >> 1) & 7 so 16 consecutive rows at one chunk hit
@@ -169,7 +169,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
                                                       int Nout, int half) {
   __shared__ __attribute__((aligned(1024))) char smem[kRing];
   __shared__ int mt_start[kMaxGroups + 1];
-  __shared__ long long s_cost[kMaxGroups + 1];
+  // the cost prefix is only needed for the XCD split below, before the first tile's
+  // loads overwrite the ring (they follow a barrier), so it borrows the ring's memory
+  long long* s_cost = reinterpret_cast<long long*>(smem);
+  static_assert(sizeof(long long) * (kMaxGroups + 1) <= kRing, "cost prefix fits the ring");
   build_schedule(offsets, NG, BM, mt_start);
   const int nt = kSwiglu ? half / 128 : (Nout + BN - 1) / BN;
   build_costs(offsets, mt_start, NG, BM, nt, s_cost);

@@ -34,7 +34,7 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kARow = BK * 2;         // K-inner operand: 128-byte rows
 constexpr int kORow = BN * 2;         // K-outer operand: 512-byte rows (64 k-rows)
 constexpr int kOStage = BK * kORow;   // 32 KiB
-constexpr int kRing = 3 * (128 * kARow + kOStage);  // 144 KiB
+constexpr int kRing = 3 * (160 * kARow + kOStage);  // 156 KiB: 3 stages up to 160 A rows
 
 __device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
 
@@ -148,7 +148,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nn_bf16(
     int I) {
   __shared__ __attribute__((aligned(1024))) char smem[kRing];
   __shared__ int mt_start[kMaxGroups + 1];
-  __shared__ long long s_cost[kMaxGroups + 1];
+  // the cost prefix is only needed for the XCD split, before the first tile's loads
+  // overwrite the ring (they follow a barrier), so it borrows the ring's memory
+  long long* s_cost = reinterpret_cast<long long*>(smem);
+  static_assert(sizeof(long long) * (kMaxGroups + 1) <= kRing, "cost prefix fits the ring");
   build_schedule(offsets, NG, BM, mt_start);
   const int nt = (N + BN - 1) / BN;
   build_costs(offsets, mt_start, NG, BM, nt, s_cost);
@@ -177,11 +180,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nn_bf16(
     const int n0 = tl.n_idx * BN;
     const bool w_on = 64 * wm < m_rows && n0 + 128 * wn < N;
     const bool w_sub1 = 64 * wm + 32 < m_rows;
+    // three stages when an A stage of the rows rounded up to 16 fits three times
+    // (up to 160 rows), else two of nA*64 rows; A rows past the expert's end that are not
+    // loaded only feed output rows that are not stored
     const int nA = (m_rows + 63) >> 6;
-    const int sA = nA * 64 * kARow;
+    const int rA16 = (m_rows + 15) & ~15;
+    const bool three = 3 * (rA16 * kARow + kOStage) <= kRing;
+    const int rowsA = three ? rA16 : nA * 64;
+    const int sA = rowsA * kARow;
     const int sStage = sA + kOStage;
-    const int nst = (3 * sStage <= kRing) ? 3 : 2;
-    const int per_stage = nA + 4;
+    const int nst = three ? 3 : 2;
+    const int nAw = __builtin_amdgcn_readfirstlane((rowsA - 8 * wv + 63) >> 6);
+    const int per_stage = nAw + 4;
 
     const i32x4 arsrc = buffer_rsrc(A + (int64_t)(row0 + m0) * Kd, (uint32_t)m_rows * Kd * 2);
     uint32_t aoff[4];
@@ -198,10 +208,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nn_bf16(
   {                                                                                   \
     const uint32_t sa_ = ldsw + (st) * sStage;                                        \
     const uint32_t ko_ = (uint32_t)(kt) * kARow;                                      \
-    load16_to_lds(arsrc, sa_, aoff[0] + ko_);                                         \
-    if (nA > 1) load16_to_lds(arsrc, sa_ + 64 * kARow, aoff[1] + ko_);                \
-    if (nA > 2) load16_to_lds(arsrc, sa_ + 128 * kARow, aoff[2] + ko_);               \
-    if (nA > 3) load16_to_lds(arsrc, sa_ + 192 * kARow, aoff[3] + ko_);               \
+    if (nAw > 0) load16_to_lds(arsrc, sa_, aoff[0] + ko_);                            \
+    if (nAw > 1) load16_to_lds(arsrc, sa_ + 64 * kARow, aoff[1] + ko_);               \
+    if (nAw > 2) load16_to_lds(arsrc, sa_ + 128 * kARow, aoff[2] + ko_);              \
+    if (nAw > 3) load16_to_lds(arsrc, sa_ + 192 * kARow, aoff[3] + ko_);              \
     kouter_issue(bl, lds0 + (st) * sStage + sA, wv, (kt) * BK, Kd, N, 0, nullptr);    \
   }
 

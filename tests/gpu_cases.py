@@ -23,6 +23,9 @@ SMALL_CASES = {
     # T >= 2048 with a shared expert: its gate/up GEMM runs as a dense launch (ragged
     # last row tile; dense-fp8 below is the FP8 counterpart)
     "dense-bf16": ("v3-bf16", dict(T=2100, H=384, E=16, G=4, M=2, K=4, J=2, I=384)),
+    # above 3072 tokens the router's logits kernel gives each wave four experts: a ragged
+    # last 64-token block and E = 48 (not a multiple of the 32 experts per workgroup)
+    "re4-ragged-bf16": ("v3-bf16", dict(T=3137, H=256, E=48, G=4, M=2, K=4, J=2, I=128)),
     "ragged-fp8": ("v3-fp8", dict(T=700, H=384, E=16, G=4, M=2, K=4, J=2, I=256)),
     "dense-fp8": ("v3-fp8", dict(T=2100, H=384, E=16, G=4, M=2, K=4, J=2, I=256)),
     "v3route-fp8": ("v3-fp8", dict(T=300, H=256, I=256)),

@@ -15,6 +15,9 @@ SMALL_CASES = {
     "tiny-fp32": ("tiny-fp32", {}),
     "tiny-fp32-T1": ("tiny-fp32", dict(T=1)),
     "ragged-bf16": ("v3-bf16", dict(T=1000, H=384, E=16, G=4, M=2, K=4, J=2, I=256)),
+    # ~150 rows per expert: the grouped GEMMs' three-stage ring with A stages of up to
+    # 160 rows (rows rounded up to 16), next to experts just above it
+    "rows150-bf16": ("v3-bf16", dict(T=600, H=384, E=16, G=4, M=2, K=4, J=2, I=256)),
     "v3route-bf16": ("v3-bf16", dict(T=513, H=256, I=128)),
     "noshared-bf16": ("v3-bf16", dict(T=300, H=256, E=32, G=4, M=2, K=6, J=2, I=128, S=0)),
     "k1-j1-bf16": ("v3-bf16", dict(T=257, H=128, E=8, G=2, M=1, K=1, J=1, I=128)),

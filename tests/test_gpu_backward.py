@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 CASES = ["tiny-fp32", "tiny-fp32-T1", "ragged-bf16", "v3route-bf16", "noshared-bf16",
-         "k1-j1-bf16", "maxE-bf16", "dense-bf16"]
+         "k1-j1-bf16", "maxE-bf16", "dense-bf16", "rows150-bf16"]
 
 
 @pytest.fixture(scope="module", autouse=True)

@@ -74,6 +74,8 @@ def _declare(L):
     L.oracle_combine.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp, i32]
     L.oracle_combine.restype = None
     L.oracle_bias_update.argtypes = [i32, i64, i32, vp, f32, vp]
+    L.oracle_seq_load_stats.argtypes = [i64, i32, i32, vp, i32, vp, vp, vp, vp]
+    L.oracle_seq_load_stats.restype = None
     L.oracle_bias_update.restype = None
     L.oracle_combine_backward.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32]
     L.oracle_combine_backward.restype = None
@@ -314,6 +316,26 @@ def bias_update(counts, T, K, gamma, bias):
 
 
 # --- whole-layer composition ---------------------------------------------------
+
+def seq_load_stats(topk_idx, E, seq_offsets):
+    """Sequence-wise loads (mpbf.cn section 2.2, the sequence-level balance term; the
+    pages give it no formula, so only its loads are computed).  Sequence s is tokens
+    seq_offsets[s] .. seq_offsets[s+1]-1.  Returns counts [n_seq, E] int32 (chosen
+    indices per sequence and expert), stats [n_seq, 3] int32 (max count, min count,
+    experts with no token) and ratio [n_seq] fp32 = max / (L*K/E), 0 for an empty
+    sequence."""
+    idx = _c(topk_idx, np.int32)
+    off = _c(np.asarray(seq_offsets, dtype=np.int32), np.int32)
+    T, K = idx.shape
+    n = len(off) - 1
+    assert n >= 1 and off[0] == 0 and off[-1] == T and np.all(np.diff(off) >= 0)
+    assert idx.min() >= 0 and idx.max() < E
+    counts = np.empty((n, E), np.int32)
+    stats = np.empty((n, 3), np.int32)
+    ratio = np.empty((n,), np.float32)
+    lib().oracle_seq_load_stats(T, E, K, _p(idx), n, _p(off), _p(counts), _p(stats), _p(ratio))
+    return counts, stats, ratio
+
 
 def forward(x, w_router, bias, w13, w2, G, M, K, J, shared=1, expert_dtype=None,
             w13_q=None, w13_s=None, w2_q=None, w2_s=None, nthreads=None):

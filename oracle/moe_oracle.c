@@ -549,6 +549,43 @@ void oracle_bias_update(int E, int64_t T, int K, const int32_t* counts, float ga
 }
 
 /* ------------------------------------------------------------------------- */
+/* Sequence-wise load statistic [mpbf section 2.2: next to the bias rule, a     */
+/* sequence-level balance term with a very small weight keeps any one sequence  */
+/* from extreme imbalance.  The pages give that term no formula, so only the    */
+/* loads it would be built from are computed: per (sequence, expert) counts of  */
+/* the chosen indices, and per sequence the largest and smallest count, the     */
+/* number of experts with no token, and max / mean, the mean being the uniform  */
+/* share L*K/E of the sequence's L tokens].                                     */
+/* Sequence s holds tokens seq_off[s] .. seq_off[s+1]-1 (seq_off nondecreasing, */
+/* seq_off[0] = 0, seq_off[n_seq] = T).  ratio = (float)(max*E) / (float)(L*K), */
+/* one IEEE division of two exactly converted integers (below 2^24); 0 when the */
+/* sequence is empty.                                                           */
+/* ------------------------------------------------------------------------- */
+
+void oracle_seq_load_stats(int64_t T, int E, int K, const int32_t* topk_idx, int n_seq,
+                           const int32_t* seq_off, int32_t* counts, int32_t* stats,
+                           float* ratio) {
+  (void)T;
+  for (int s = 0; s < n_seq; ++s) {
+    int32_t* c = counts + (int64_t)s * E;
+    for (int e = 0; e < E; ++e) c[e] = 0;
+    for (int64_t t = seq_off[s]; t < seq_off[s + 1]; ++t)
+      for (int k = 0; k < K; ++k) c[topk_idx[t * K + k]] += 1;
+    int32_t mx = c[0], mn = c[0], zeros = 0;
+    for (int e = 0; e < E; ++e) {
+      if (c[e] > mx) mx = c[e];
+      if (c[e] < mn) mn = c[e];
+      if (c[e] == 0) zeros += 1;
+    }
+    stats[s * 3 + 0] = mx;
+    stats[s * 3 + 1] = mn;
+    stats[s * 3 + 2] = zeros;
+    const int64_t L = (int64_t)seq_off[s + 1] - seq_off[s];
+    ratio[s] = L > 0 ? (float)((int64_t)mx * E) / (float)(L * K) : 0.0f;
+  }
+}
+
+/* ------------------------------------------------------------------------- */
 /* Array forms of the scalar routines (for tests that sweep many values).     */
 /* ------------------------------------------------------------------------- */
 

@@ -206,6 +206,24 @@ moe_status moe_combine(const moe_problem* p, const void* y_sorted, const int32_t
 moe_status moe_bias_update(const moe_problem* p, const int32_t* expert_counts, float gamma,
                            float* bias, void* stream);
 
+/* Sequence-wise load statistic (mpbf.cn section 2.2: next to the bias rule, a
+ * sequence-level balance term with a very small weight keeps any single sequence from
+ * extreme imbalance; the pages give that term no formula, so this reports the loads
+ * it is built from).  Sequence s holds tokens seq_offsets[s] .. seq_offsets[s+1]-1.
+ *   topk_idx    [T,K] int32 from moe_route
+ *   seq_offsets [n_seq+1] int32: 0 = seq_offsets[0] <= ... <= seq_offsets[n_seq] = T
+ *               (empty sequences allowed)
+ *   seq_counts  [n_seq,E] int32 out: tokens of sequence s routed to expert e
+ *   seq_stats   [n_seq,3] int32 out: max count, min count, experts with no token
+ *   seq_ratio   [n_seq]   fp32  out: max / (L*K/E) for the sequence's L tokens, as
+ *               (float)(max*E) / (float)(L*K) with one IEEE division; 0 if L = 0.
+ * Limits (checked): 1 <= n_seq <= 2^24, n_seq*E < 2^31.  Offsets that break the
+ * ordering above, or indices outside [0,E), give unspecified counts but every write
+ * stays inside the outputs.  Bit-for-bit reproducible (integer atomics). */
+moe_status moe_seq_load_stats(const moe_problem* p, const int32_t* topk_idx,
+                              const int32_t* seq_offsets, int32_t n_seq, int32_t* seq_counts,
+                              int32_t* seq_stats, float* seq_ratio, void* stream);
+
 /* ---------------- backward of the layer (bf16 and fp32 paths) ----------------
  * The derivative of the forward above.  The pages fix only that the routing bias
  * takes no part in back-propagation (blog.resmic.cn section 核心架构三) and that

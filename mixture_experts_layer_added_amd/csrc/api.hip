@@ -315,6 +315,23 @@ moe_status moe_bias_update(const moe_problem* p, const int32_t* expert_counts, f
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_bias_update launch");
 }
 
+moe_status moe_seq_load_stats(const moe_problem* p, const int32_t* topk_idx,
+                              const int32_t* seq_offsets, int32_t n_seq, int32_t* seq_counts,
+                              int32_t* seq_stats, float* seq_ratio, void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  if (!topk_idx || !seq_offsets || !seq_counts || !seq_stats || !seq_ratio)
+    return fail(MOE_ERR_INVALID_ARG,
+                "topk_idx, seq_offsets, seq_counts, seq_stats and seq_ratio are required");
+  if (n_seq < 1 || n_seq > (1 << 24) || (int64_t)n_seq * d.E >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_INVALID_ARG, "n_seq=%d must be in [1, 2^24] with n_seq*E < 2^31", n_seq);
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  hipError_t e = launch_seq_load_stats(d, topk_idx, seq_offsets, n_seq, seq_counts, seq_stats,
+                                       seq_ratio, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_seq_load_stats launch");
+}
+
 static moe_status require_no_fp8(const Dims& d, const char* call) {
   if (d.expert == MOE_FP8_E4M3)
     return fail(MOE_ERR_UNSUPPORTED, "%s: the backward is built for the bf16 and fp32 paths", call);

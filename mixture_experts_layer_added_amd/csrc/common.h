@@ -106,6 +106,41 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   return static_cast<uint32_t>(w);
 }
 
+// ---- output staging through LDS (GEMM epilogues) ----
+// A wave stages a block of rows of 256 bytes in LDS and stores it back with 16-byte
+// lanes, 16 lanes per row, so every store instruction writes whole 128-byte lines.
+// The 16-byte chunk slots of a row are xor-swizzled by the row, so 32 lanes writing
+// 8 bytes at one chunk position of 32 consecutive rows, and lanes reading whole rows,
+// spread over the banks.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int stg256_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  return make_uint2((uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16),
+                    (uint32_t)f32_to_bf16_bits(c) | ((uint32_t)f32_to_bf16_bits(d) << 16));
+}
+
+// 8 bytes at byte 16*c + 8*half of staged row r
+__device__ __forceinline__ void stg256_put(char* stg, int r, int c, int half, uint2 v) {
+  *reinterpret_cast<uint2*>(stg + stg256_off(r, c) + 8 * half) = v;
+}
+
+// Staged rows 0 .. nrows-1 to out (row stride ld_bytes), non-temporally.  Waits for the
+// wave's own staging writes first and for its reads at the end, so the area can be
+// written again by the same wave; other waves must be kept off it by the caller.
+__device__ __forceinline__ void stg256_flush(const char* stg, int lane, int nrows, char* out,
+                                             int64_t ld_bytes) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const int c = lane & 15;
+  for (int r = lane >> 4; r < nrows; r += 4) {
+    const uint4 u = *reinterpret_cast<const uint4*>(stg + stg256_off(r, c));
+    const u32x4 v = {u.x, u.y, u.z, u.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + r * ld_bytes + 16 * c));
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // exp and sigmoid of the router (shared by the routing and its backward).  ln 2 is split for Cody-Waite reduction: the high part is ln 2
 // rounded to 16 significant bits (45426/65536) so k*LN2_HI is exact for |k| < 256;
@@ -189,6 +224,11 @@ hipError_t launch_combine(const Dims& d, const void* ys, const int32_t* inv_perm
 
 hipError_t launch_bias_update(const Dims& d, const int32_t* counts, float gamma, float* bias,
                               hipStream_t st);
+
+// sequence-wise loads (seqstats.hip): counts [n_seq, E], stats [n_seq, 3], ratio [n_seq]
+hipError_t launch_seq_load_stats(const Dims& d, const int32_t* idx, const int32_t* seq_off,
+                                 int n_seq, int32_t* counts, int32_t* stats, float* ratio,
+                                 hipStream_t st);
 
 hipError_t launch_quantize_weights(const uint16_t* w, uint8_t* q, float* scale, int64_t batch,
                                    int rows, int cols, hipStream_t st);

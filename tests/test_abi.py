@@ -197,3 +197,14 @@ def test_backward_entry_points_validate(L):
     assert rc == L.MOE_ERR_INVALID_ARG and "2^31" in L.last_error()
     rc = lib.moe_expert_ffn_backward_weight(ctypes.byref(big), d, None, d, d, d, d, d, d, None)
     assert rc == L.MOE_ERR_INVALID_ARG and "2^31" in L.last_error()
+
+
+@pytest.mark.parametrize("n_seq", [0, -1, (1 << 24) + 1])
+def test_seq_load_stats_rejects_bad_sequence_counts(L, n_seq):
+    lib = L.lib()
+    dummy = ctypes.c_void_p(4096)
+    p = prob(L)
+    rc = lib.moe_seq_load_stats(ctypes.byref(p), dummy, dummy, n_seq, dummy, dummy, dummy, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "n_seq" in L.last_error()
+    rc = lib.moe_seq_load_stats(ctypes.byref(p), dummy, None, 1, dummy, dummy, dummy, None)
+    assert rc == L.MOE_ERR_INVALID_ARG

@@ -142,9 +142,15 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
 //   kSwiglu: wave column wn owns gate rows 64wn..64wn+63 of the tile and the matching
 //   up rows, so each lane holds the gate and up value of the same h element and
 //   applies SwiGLU in registers.
-// Operand layout (32x32x16): lane l supplies row (l%32), k = 8*(l/32)..+7 of A and
-// column (l%32), the same k of B; result element i of lane l is row
-// 8*(i/4) + 4*(l/32) + i%4, column l%32.
+// Operand layout (32x32x16): lane l supplies row (l%32), k = 8*(l/32)..+7 of the first
+// operand and column (l%32), the same k of the second; result element i of lane l is
+// row 8*(i/4) + 4*(l/32) + i%4, column l%32.  The gate/up kernel passes the activation
+// fragment first (a lane's results: one output column, 16 rows); the down kernel passes
+// the weight fragment first, so a lane's results are one activation row (l%32) and four
+// consecutive output columns per group of four elements.  The down kernel's epilogue
+// stages each wave's 64 x 128 block of Y in the ring (16 KiB per wave, once every wave is
+// done with it) and stores it back with 16-byte lanes, so every store instruction writes
+// whole 128-byte lines.
 // ---------------------------------------------------------------------------
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kRowBytes = BK * 2;               // one row of one stage: a full 128-B line
@@ -155,6 +161,9 @@ constexpr int kRing = 3 * (160 * kRowBytes + kBStage);  // 156 KiB: 3 stages up 
 // chunk slots xor-swizzled by (row >> 1) & 7 so 16 consecutive rows at one chunk hit
 // 16 distinct bank groups
 __device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ (r >> 1)) & 7) * 16; }
+
+constexpr int kStgBytes = 64 * 256;  // one wave's staged outputs: 64 rows x 256 bytes
+static_assert(8 * kStgBytes <= kRing, "the eight waves' staging areas fit the ring");
 
 // gather != nullptr: row r of the permuted order is row gather[r] of A (a_rows rows),
 // so the activation rows are read from the unpermuted input.
@@ -204,7 +213,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
     const bool w_on = 64 * wm < m_rows && (kSwiglu || tl.n_idx * BN + 128 * wn < Nout);
     const bool w_sub1 = 64 * wm + 32 < m_rows;
     // ring shape of this tile: three stages when an A stage of the rows rounded up to 16
-    // fits three times (experts of up to 144 rows), else two stages of nA*64 rows.  A
+    // fits three times (experts of up to 160 rows), else two stages of nA*64 rows.  A
     // rows past the expert's end that are not loaded hold stale data: their products
     // land in output rows that are not stored.
     const int nA = (m_rows + 63) >> 6;
@@ -293,12 +302,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
           const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(as + swz(arow0, c));
 #pragma unroll
           for (int n = 0; n < 4; ++n)
-            acc[0][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[n], acc[0][n], 0, 0, 0);
+            acc[0][n] = kSwiglu
+                            ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[n], acc[0][n], 0, 0, 0)
+                            : __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[n], a0, acc[0][n], 0, 0, 0);
           if (w_sub1) {
             const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(as + swz(arow1, c));
 #pragma unroll
             for (int n = 0; n < 4; ++n)
-              acc[1][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[n], acc[1][n], 0, 0, 0);
+              acc[1][n] = kSwiglu
+                              ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[n], acc[1][n], 0, 0, 0)
+                              : __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[n], a1, acc[1][n], 0, 0, 0);
           }
         }
       }
@@ -306,15 +319,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
     }
 #undef STAGE_LOAD
 
-    if (w_on) {
+    if (kSwiglu) {
+      // gate/up: h (and a, u) stored straight from the accumulators, 32 lanes writing
+      // 64 contiguous bytes of a row per instruction (staging these through LDS measured
+      // 0.6% slower for this launch)
+      if (w_on) {
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          if (m >= m_rows) continue;
-          uint16_t* cp = C + (int64_t)(row0 + m0 + m) * Nout;
-          if (kSwiglu) {
+          for (int i = 0; i < 16; ++i) {
+            const int m = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            if (m >= m_rows) continue;
+            uint16_t* cp = C + (int64_t)(row0 + m0 + m) * Nout;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
               const int col = tl.n_idx * 128 + 64 * wn + 32 * t + (lane & 31);
@@ -326,13 +342,31 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(const uint16_t* __restrict
                 ap[half + col] = f32_to_bf16_bits(acc[mi][2 * t + 1][i]);
               }
             }
-          } else {
-#pragma unroll
-            for (int n = 0; n < 4; ++n)
-              __builtin_nontemporal_store(f32_to_bf16_bits(acc[mi][n][i]),
-                                          cp + tl.n_idx * BN + 128 * wn + 32 * n + (lane & 31));
           }
-        }
+      }
+    } else {
+      // down: every wave is done with the ring's stages, whose memory then stages each
+      // wave's 64 x 128 block of Y (16 KiB per wave) for whole-line stores.  Lane
+      // columns 128wn + 32n + 8ig + 4(lane/32) .. +3 of the tile go to chunk 4n + ig.
+      __syncthreads();
+      if (w_on) {
+        char* stg = smem + wv * kStgBytes;
+        const int nrows = min(64, m_rows - 64 * wm);  // rows of this wave's block (>= 1)
+        const int64_t orow = (int64_t)row0 + m0 + 64 * wm;
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int ig = 0; ig < 4; ++ig) {
+              const f32x16& v = acc[mi][n];
+              stg256_put(stg, 32 * mi + (lane & 31), 4 * n + ig, lane >> 5,
+                         pack4_bf16(v[4 * ig], v[4 * ig + 1], v[4 * ig + 2], v[4 * ig + 3]));
+            }
+        stg256_flush(stg, lane, nrows,
+                     reinterpret_cast<char*>(C + orow * Nout + tl.n_idx * BN + 128 * wn),
+                     (int64_t)Nout * 2);
+      }
     }
   }
 }

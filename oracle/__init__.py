@@ -70,6 +70,9 @@ def _declare(L):
                                  vp, vp]
     L.oracle_permute.restype = i32
     L.oracle_expert_ffn.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, i32]
+    L.oracle_expert_ffn_h.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp,
+                                      vp, i32]
+    L.oracle_expert_ffn_h.restype = i32
     L.oracle_expert_ffn.restype = i32
     L.oracle_combine.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp, i32]
     L.oracle_combine.restype = None
@@ -273,8 +276,10 @@ def permute(x, topk_idx, counts, E, shared=1, out_dtype=None):
 
 
 def expert_ffn(x_rows, w13, w2, out_dtype, x_scale=None, w13_scale=None, w2_scale=None,
-               nthreads=None):
-    """One expert on a block of rows.  x_rows [n,H]; w13 [2I,H]; w2 [H,I]."""
+               nthreads=None, want_h=False):
+    """One expert on a block of rows.  x_rows [n,H]; w13 [2I,H]; w2 [H,I].  Returns y,
+    or with want_h (y, h, h_scale): h [n,I] as stored between the GEMMs (E4M3 codes and
+    h_scale [n,I/128] for the FP8 path, else h_scale None)."""
     x_rows = np.ascontiguousarray(x_rows)
     w13 = np.ascontiguousarray(w13)
     w2 = np.ascontiguousarray(w2)
@@ -287,12 +292,21 @@ def expert_ffn(x_rows, w13, w2, out_dtype, x_scale=None, w13_scale=None, w2_scal
         x_scale = _c(x_scale, np.float32)
         w13_scale = _c(w13_scale, np.float32)
         w2_scale = _c(w2_scale, np.float32)
-    rc = lib().oracle_expert_ffn(n, H, I, dt, _p(x_rows), _p(x_scale), _p(w13), _p(w13_scale),
-                                 _p(w2), _p(w2_scale), out_dtype, _p(y),
-                                 nthreads or default_threads())
+    if not want_h:
+        rc = lib().oracle_expert_ffn(n, H, I, dt, _p(x_rows), _p(x_scale), _p(w13),
+                                     _p(w13_scale), _p(w2), _p(w2_scale), out_dtype, _p(y),
+                                     nthreads or default_threads())
+        if rc != 0:
+            raise ValueError(f"oracle_expert_ffn rejected the input (code {rc})")
+        return y
+    h = np.empty((n, I), x_rows.dtype)
+    h_scale = np.empty((n, I // 128), np.float32) if dt == E4M3 else None
+    rc = lib().oracle_expert_ffn_h(n, H, I, dt, _p(x_rows), _p(x_scale), _p(w13),
+                                   _p(w13_scale), _p(w2), _p(w2_scale), out_dtype, _p(y), _p(h),
+                                   _p(h_scale), nthreads or default_threads())
     if rc != 0:
-        raise ValueError(f"oracle_expert_ffn rejected the input (code {rc})")
-    return y
+        raise ValueError(f"oracle_expert_ffn_h rejected the input (code {rc})")
+    return y, h, h_scale
 
 
 def combine(y_sorted, inv_perm, topk_gate, T, shared=1, nthreads=None):
@@ -410,8 +424,9 @@ def router_backward(x, w_router, logits, topk_idx, topk_gate, dgate, nthreads=No
     return dz, dxr, dwr
 
 
-def expert_backward(x_rows, w13, w2, dy_rows, nthreads=None):
-    """One expert on a block of rows.  Returns (h, dau, dx_rows, dw13 f32, dw2 f32)."""
+def expert_backward(x_rows, w13, w2, dy_rows, nthreads=None, weights=True):
+    """One expert on a block of rows.  Returns (h, dau, dx_rows, dw13 f32, dw2 f32);
+    weights=False computes the input part only (dw13, dw2 are then None)."""
     x_rows = np.ascontiguousarray(x_rows)
     w13 = np.ascontiguousarray(w13)
     w2 = np.ascontiguousarray(w2)
@@ -422,8 +437,8 @@ def expert_backward(x_rows, w13, w2, dy_rows, nthreads=None):
     h = np.empty((n, I), x_rows.dtype)
     dau = np.empty((n, 2 * I), x_rows.dtype)
     dx = np.empty((n, H), x_rows.dtype)
-    dw13 = np.empty((2 * I, H), np.float32)
-    dw2 = np.empty((H, I), np.float32)
+    dw13 = np.empty((2 * I, H), np.float32) if weights else None
+    dw2 = np.empty((H, I), np.float32) if weights else None
     rc = lib().oracle_expert_backward(n, H, I, dt, _p(x_rows), _p(w13), _p(w2), _p(dy_rows),
                                       _p(h), _p(dau), _p(dx), _p(dw13), _p(dw2),
                                       nthreads or default_threads())

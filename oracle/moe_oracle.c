@@ -430,6 +430,7 @@ typedef struct {
   const void* w13; const float* w13_scale;
   const void* w2; const float* w2_scale;
   void* y;
+  void* h_out; float* h_scale_out; /* optional copies of the stored h (NULL: not kept) */
 } ffn_ctx;
 
 static double dot_blocked(const ffn_ctx* F, const void* a, const float* a_scale, int64_t a_row,
@@ -480,6 +481,11 @@ static void ffn_item(void* c, int64_t r) {
     hs = malloc(4 * (size_t)I);
     for (int n = 0; n < I; ++n) ((float*)hs)[n] = oracle_f32_from_f64(h[n]);
   }
+  if (F->h_out) {
+    const size_t es = F->dtype == DT_E4M3 ? 1 : (F->dtype == DT_BF16 ? 2 : 4);
+    memcpy((char*)F->h_out + (size_t)r * I * es, hs, es * (size_t)I);
+    if (hscale) memcpy(F->h_scale_out + r * (I / 128), hscale, sizeof(float) * (I / 128));
+  }
   for (int m = 0; m < H; ++m) {
     double y = dot_blocked(F, hs, hscale, 0, F->w2, F->w2_scale, m, I, I / 128);
     if (F->out_dtype == DT_BF16) ((uint16_t*)F->y)[r * H + m] = oracle_bf16_from_f64(y);
@@ -495,7 +501,19 @@ int oracle_expert_ffn(int64_t n_rows, int H, int I, int dtype, const void* x,
                       const void* w2, const float* w2_scale, int out_dtype, void* y,
                       int nthreads) {
   if (dtype == DT_E4M3 && (H % 128 || I % 128)) return -1;
-  ffn_ctx c = {H, I, dtype, out_dtype, x, x_scale, w13, w13_scale, w2, w2_scale, y};
+  ffn_ctx c = {H, I, dtype, out_dtype, x, x_scale, w13, w13_scale, w2, w2_scale, y, NULL, NULL};
+  parallel_for(n_rows, nthreads, ffn_item, &c);
+  return 0;
+}
+
+/* The same, also returning h as stored between the two GEMMs: h [n_rows, I] at the
+ * activation dtype (E4M3 codes with h_scale [n_rows, I/128] for the FP8 path). */
+int oracle_expert_ffn_h(int64_t n_rows, int H, int I, int dtype, const void* x,
+                        const float* x_scale, const void* w13, const float* w13_scale,
+                        const void* w2, const float* w2_scale, int out_dtype, void* y,
+                        void* h, float* h_scale, int nthreads) {
+  if (dtype == DT_E4M3 && (H % 128 || I % 128)) return -1;
+  ffn_ctx c = {H, I, dtype, out_dtype, x, x_scale, w13, w13_scale, w2, w2_scale, y, h, h_scale};
   parallel_for(n_rows, nthreads, ffn_item, &c);
   return 0;
 }
@@ -810,6 +828,7 @@ int oracle_expert_backward(int64_t n, int H, int I, int dtype, const void* x, co
   if (dtype == DT_E4M3) return -1;
   ebwd_ctx b = {H, I, dtype, x, w13, w2, dy, h, dau, dx};
   parallel_for(n, nthreads, ebwd_row_item, &b);
+  if (!dw13 && !dw2) return 0; /* input part only */
   ewgrad_ctx w = {n, H, I, dtype, x, dy, h, dau, dw13, dw2};
   parallel_for(2 * I + H, nthreads, ewgrad_item, &w);
   return 0;

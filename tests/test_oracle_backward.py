@@ -172,3 +172,22 @@ def test_local_decompositions_match_full_backward(act):
             assert np.array_equal(r["dw13_a"], bw["dw13"][g][n])
             assert np.array_equal(r["dw13_u"], bw["dw13"][g][I + n])
             assert np.array_equal(r["dau"], bw["dau"][off[g]:off[g + 1]][:, [n, I + n]])
+
+
+def test_input_part_alone_equals_the_full_expert_backward():
+    """expert_backward(weights=False) skips the weight gradients only: h, [da|du] and dx
+    are bit for bit those of the full call."""
+    rng = np.random.default_rng(21)
+    n, H, I = 7, 256, 128
+    for act in ("f32", "bf16"):
+        def mk(shape, std):
+            v = rng.standard_normal(shape) * std
+            return (oracle.bf16_from_f64_array(v).reshape(shape) if act == "bf16"
+                    else v.astype(np.float32))
+        x, dy = mk((n, H), 1.0), mk((n, H), 1.0)
+        w13, w2 = mk((2 * I, H), 0.05), mk((H, I), 0.05)
+        full = oracle.expert_backward(x, w13, w2, dy)
+        part = oracle.expert_backward(x, w13, w2, dy, weights=False)
+        assert part[3] is None and part[4] is None
+        for a, b in zip(full[:3], part[:3]):
+            assert np.array_equal(a, b)

@@ -205,6 +205,44 @@ def test_ffn_fp8_against_dequantised_float64(orc):
     assert np.abs(yf - ref).max() <= 2 ** -8 * np.abs(ref).max()
 
 
+def test_ffn_returns_the_stored_h(orc):
+    """expert_ffn(want_h=True) hands back h as stored between the GEMMs: y is the same
+    as without it, and h matches float64 numpy SwiGLU rounded like the layer stores it
+    (bf16; E4M3 codes + per-128 scales from the oracle's own activation quantiser, which
+    has its own pins), so a GPU test can compare the gate/up output directly."""
+    rng = np.random.default_rng(10)
+    n, H, I = 6, 256, 256
+    xb = orc.bf16_from_f64_array(rng.standard_normal((n, H))).reshape(n, H)
+    w13b = orc.bf16_from_f64_array(rng.standard_normal((2 * I, H)) * 0.05).reshape(2 * I, H)
+    w2b = orc.bf16_from_f64_array(rng.standard_normal((H, I)) * 0.05).reshape(H, I)
+    y0 = orc.expert_ffn(xb, w13b, w2b, orc.BF16)
+    y, h, hs = orc.expert_ffn(xb, w13b, w2b, orc.BF16, want_h=True)
+    assert np.array_equal(y, y0) and hs is None and h.dtype == np.uint16
+    x, w13 = (orc.bf16_to_f32(v).astype(np.float64) for v in (xb, w13b))
+    a, u = x @ w13[:I].T, x @ w13[I:].T
+    href = a / (1.0 + np.exp(-a)) * u
+    hf = orc.bf16_to_f32(h).astype(np.float64)
+    assert np.all(np.abs(hf - href) <= np.abs(href) * 2 ** -8 + 1e-12)
+    # FP8: codes and scales of h are those of quantising the float64 h per 128 columns
+    qx, sx = orc.quantize_act_fp8(xb)
+    q13, s13 = orc.quantize_weight_fp8(w13b)
+    q2, s2 = orc.quantize_weight_fp8(w2b)
+    y8 = orc.expert_ffn(qx, q13, q2, orc.BF16, sx, s13, s2)
+    y8h, hq, hsc = orc.expert_ffn(qx, q13, q2, orc.BF16, sx, s13, s2, want_h=True)
+    assert np.array_equal(y8, y8h) and hq.dtype == np.uint8 and hsc.shape == (n, I // 128)
+
+    def deq(q):
+        return torch.from_numpy(np.ascontiguousarray(q)).view(torch.float8_e4m3fn).double().numpy()
+
+    xd = deq(qx) * np.repeat(sx, 128, axis=1)
+    w13d = deq(q13) * np.kron(s13, np.ones((128, 128)))
+    a8, u8 = xd @ w13d[:I].T, xd @ w13d[I:].T
+    h8 = a8 / (1.0 + np.exp(-a8)) * u8
+    assert np.allclose(hsc, np.abs(h8).reshape(n, -1, 128).max(axis=2) / 448.0, rtol=1e-6)
+    hd = deq(hq) * np.repeat(hsc, 128, axis=1)
+    assert np.abs(hd - h8).max() <= 2 ** -3 * np.abs(h8).max()
+
+
 # --------------------------------------------------------------------------- combine
 
 def test_combine_identity_experts(orc):

@@ -109,8 +109,13 @@ moe_status moe_route(const moe_problem* p, const void* x, const float* w_router,
  * order; within an expert, tokens ascend; the shared expert (S = 1) is the last group
  * and holds every token in order.
  *   x            [T,H] act_dtype
- *   topk_idx     [T,K] int32   from moe_route (values outside [0,E) are skipped and
- *                              their inv_perm entry is -1; the layout is then undefined)
+ *   topk_idx     [T,K] int32   from moe_route; every value must lie in [0,E) (moe_route
+ *                              only writes such values).  A pair outside it is skipped
+ *                              and its inv_perm entry is -1 (writes stay in bounds);
+ *                              offsets[E] is then T*K less the skipped pairs, and the
+ *                              calls that read the shared rows at T*K + t (the FFN's
+ *                              dense shared launch, the combine, the backward) are not
+ *                              defined for such input
  *   offsets      [E+S+1] int32 out  first row of each group; offsets[E] = T*K
  *   sorted_token [R]     int32 out  token of each row
  *   inv_perm     [T,K]   int32 out  row holding (t, topk_idx[t,k])

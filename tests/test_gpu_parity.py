@@ -218,9 +218,14 @@ def test_forward_end_to_end(name):
     e1 = rel_err(as_f64(np_(layer.y_sorted), w.act), ys_ref)
     # y = Y_shared + sum_k g_k Y_k with sum_k g_k = 1, so an expert-output error of at
     # most tol*max|Y| moves y by at most 2*tol*max|Y|
-    dy = np.abs(as_f64(np_(y), w.act) - as_f64(ref["y"], w.act)).max()
+    y_ref = as_f64(ref["y"], w.act)
+    dy = np.abs(as_f64(np_(y), w.act) - y_ref).max()
     e2 = float(dy / (2 * np.abs(ys_ref).max()))
-    log(f"    y_sorted rel err {e1:.3e}, y err / (2 max|Y|) {e2:.3e} (bound {TOL[w.expert]})")
+    # y's own normwise error (reported, not bounded: with FP8 experts it can exceed the
+    # expert-output tolerance because y is smaller than the rows it sums)
+    e3 = float(dy / np.abs(y_ref).max())
+    log(f"    y_sorted rel err {e1:.3e}, y err / (2 max|Y|) {e2:.3e} (bound {TOL[w.expert]}); "
+        f"y err / max|y| {e3:.3e}")
     assert e1 <= TOL[w.expert] and e2 <= TOL[w.expert]
 
 

@@ -33,7 +33,8 @@
  *     (a per-thread string).
  *   - Outputs are overwritten entirely; the only in/out argument is `bias`.
  *   - Calls that share no output buffers may run concurrently on different streams; the
- *     library keeps no mutable global state apart from the per-thread error string.
+ *     library keeps no mutable global state apart from the per-thread error string and
+ *     the scratch array of moe_permute_noalloc (see there).
  *
  * Problem limits (checked): 1 <= T, T*(K+1) < 2^31; H % 128 == 0, 128 <= H <= 65536;
  * I % 128 == 0, 128 <= I <= 32768, H*I <= 2^28 (one expert's weights addressed with
@@ -131,6 +132,18 @@ moe_status moe_permute(const moe_problem* p, const void* x, const int32_t* topk_
                        int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm,
                        void* x_sorted, float* x_sorted_scale, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* moe_permute without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, outputs and results as moe_permute, bit for bit; the
+ * scratch lives in a fixed 8 MiB device array inside the library, one per GPU, held
+ * until the process ends.  The call allocates nothing.
+ * Limit (checked, else MOE_ERR_WORKSPACE): T*K + 2*ceil(T/256)*E <= 2,097,088.
+ * Calls that overlap in time on one GPU (different streams, host threads) share that
+ * array and race: serialise them.  Nothing in the array needs clearing between calls. */
+moe_status moe_permute_noalloc(const moe_problem* p, const void* x, const int32_t* topk_idx,
+                               int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm,
+                               void* x_sorted, float* x_sorted_scale, void* stream);
 
 /* Expert FFNs (SwiGLU) of every group as one grouped GEMM pair:
  *   h = silu(x W13[g][0:I]^T) * (x W13[g][I:2I]^T),  Y = h W2[g]^T,

@@ -22,7 +22,8 @@ EXPORTS = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_up",
            "moe_combine", "moe_bias_update", "moe_quantize_weights_fp8", "moe_workspace_bytes",
            "moe_status_str", "moe_last_error", "moe_expert_ffn_up_save", "moe_combine_backward",
            "moe_router_backward", "moe_expert_ffn_backward_input",
-           "moe_expert_ffn_backward_weight", "moe_unpermute_sum", "moe_seq_load_stats")
+           "moe_expert_ffn_backward_weight", "moe_unpermute_sum", "moe_permute_noalloc",
+           "moe_seq_load_stats")
 
 
 class MoeError(RuntimeError):
@@ -58,6 +59,7 @@ def lib():
         pp = ctypes.POINTER(moe_problem)
         L.moe_route.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_permute.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_permute_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_seq_load_stats.argtypes = [pp, vp, vp, i32, vp, vp, vp, vp]
         L.moe_expert_ffn.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_expert_ffn_up.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -84,7 +86,7 @@ def lib():
                   "moe_combine", "moe_bias_update", "moe_quantize_weights_fp8",
                   "moe_expert_ffn_up_save", "moe_combine_backward", "moe_router_backward",
                   "moe_expert_ffn_backward_input", "moe_expert_ffn_backward_weight",
-                  "moe_unpermute_sum", "moe_seq_load_stats"):
+                  "moe_unpermute_sum", "moe_permute_noalloc", "moe_seq_load_stats"):
             getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -137,6 +139,14 @@ def moe_permute(p, x, topk_idx, offsets, sorted_token, inv_perm, x_sorted, x_sor
                              _ptr(sorted_token), _ptr(inv_perm), _ptr(x_sorted),
                              _ptr(x_sorted_scale), _ptr(ws), ws_bytes, _stream(stream)),
            "moe_permute")
+
+
+def moe_permute_noalloc(p, x, topk_idx, offsets, sorted_token, inv_perm, x_sorted,
+                        x_sorted_scale=None, stream=None):
+    _check(lib().moe_permute_noalloc(ctypes.byref(p), _ptr(x), _ptr(topk_idx), _ptr(offsets),
+                                     _ptr(sorted_token), _ptr(inv_perm), _ptr(x_sorted),
+                                     _ptr(x_sorted_scale), _stream(stream)),
+           "moe_permute_noalloc")
 
 
 def moe_seq_load_stats(p, topk_idx, seq_offsets, n_seq, seq_counts, seq_stats, seq_ratio,

@@ -179,6 +179,35 @@ moe_status moe_permute(const moe_problem* p, const void* x, const int32_t* topk_
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_permute launch");
 }
 
+moe_status moe_permute_noalloc(const moe_problem* p, const void* x, const int32_t* topk_idx,
+                               int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm,
+                               void* x_sorted, float* x_sorted_scale, void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  if (!topk_idx || !offsets || !sorted_token || !inv_perm)
+    return fail(MOE_ERR_INVALID_ARG, "topk_idx, offsets, sorted_token and inv_perm are required");
+  if (x_sorted) {  // NULL: index maps only
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(x_sorted);
+    if (d.expert == MOE_FP8_E4M3 && !x_sorted_scale)
+      return fail(MOE_ERR_INVALID_ARG, "x_sorted_scale is required for the FP8 path");
+  }
+  if (permute_ws_bytes(d) > permute_scratch_capacity())
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_permute_noalloc: this problem needs %zu scratch bytes, the library holds "
+                "%zu (T*K + 2*ceil(T/256)*E must be at most %zu); use moe_permute",
+                permute_ws_bytes(d), permute_scratch_capacity(),
+                (permute_scratch_capacity() - 256) / sizeof(int32_t));
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  void* ws = nullptr;
+  hipError_t e = permute_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "moe_permute_noalloc: device address of the scratch");
+  e = launch_permute(d, x, topk_idx, offsets, sorted_token, inv_perm, x_sorted, x_sorted_scale,
+                     ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_permute_noalloc launch");
+}
+
 moe_status moe_expert_ffn_up(const moe_problem* p, const void* x_sorted,
                              const float* x_sorted_scale, const int32_t* offsets,
                              const void* w13, const float* w13_scale, void* h, float* h_scale,

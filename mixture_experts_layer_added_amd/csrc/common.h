@@ -184,6 +184,10 @@ hipError_t launch_route(const Dims& d, const void* x, const float* w_router, con
                         hipStream_t st);
 
 size_t permute_ws_bytes(const Dims& d);
+// The permute's device-resident scratch (moe_permute_noalloc): its size, and its device
+// address on the current device (looked up once per device).
+size_t permute_scratch_capacity();
+hipError_t permute_scratch(void** ptr);
 // x_sorted == nullptr: only offsets, sorted_token and inv_perm are written
 hipError_t launch_permute(const Dims& d, const void* x, const int32_t* idx, int32_t* offsets,
                           int32_t* sorted_token, int32_t* inv_perm, void* x_sorted,

@@ -14,9 +14,20 @@
 //      k_perm_index:   the index maps alone, when the expert GEMM gathers its rows
 //                      from x itself (then FP8 quantises each token once, in
 //                      k_quant_act).
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
+
+// Scratch of moe_permute_noalloc: the per-pair ranks and the per-block expert counts and
+// offsets that moe_permute keeps in the caller's workspace, in a fixed device array
+// instead (one copy per GPU, held until the process ends).  Host code never passes
+// `scratch` itself to a kernel: its device address comes from hipGetSymbolAddress,
+// taken once per device with that device current.
+constexpr size_t kPermuteScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) char scratch[kPermuteScratchBytes];
+
 namespace {
 
 constexpr int kBlockTok = 256;  // tokens per histogram block (4 waves)
@@ -233,6 +244,30 @@ hipError_t launch_quantize_act(const Dims& d, const uint16_t* x, uint8_t* xq, fl
 size_t permute_ws_bytes(const Dims& d) {
   const int64_t nb = (d.T + kBlockTok - 1) / kBlockTok;
   return sizeof(int32_t) * (size_t)(d.T * d.K + 2 * nb * d.E) + 256;
+}
+
+size_t permute_scratch_capacity() { return kPermuteScratchBytes; }
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void* g_scratch_ptr[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+}  // namespace
+
+hipError_t permute_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_permute(const Dims& d, const void* x, const int32_t* idx, int32_t* offsets,

@@ -199,6 +199,25 @@ def test_backward_entry_points_validate(L):
     assert rc == L.MOE_ERR_INVALID_ARG and "2^31" in L.last_error()
 
 
+def test_noalloc_permute_rejects_problems_beyond_its_scratch(L):
+    """moe_permute_noalloc holds its scratch in a fixed 8 MiB array: problems whose
+    index scratch (T*K + 2*ceil(T/256)*E int32) exceeds it are refused before any launch,
+    with MOE_ERR_WORKSPACE and a message naming the limit."""
+    lib = L.lib()
+    dummy = ctypes.c_void_p(4096)
+    # 2^20 tokens x 8: 8.4M ranks alone, over the 2,097,088-entry limit
+    p = prob(L, T=1 << 20, K=8, E=256, G=8, M=4, J=2, H=256, I=128, act_dtype=1, expert_dtype=1)
+    rc = lib.moe_permute_noalloc(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, None, None,
+                                 None)
+    assert rc == L.MOE_ERR_WORKSPACE
+    assert "2097088" in L.last_error() and "moe_permute" in L.last_error()
+    # required index-map pointers
+    p = prob(L)
+    rc = lib.moe_permute_noalloc(ctypes.byref(p), dummy, None, dummy, dummy, dummy, None, None,
+                                 None)
+    assert rc == L.MOE_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("n_seq", [0, -1, (1 << 24) + 1])
 def test_seq_load_stats_rejects_bad_sequence_counts(L, n_seq):
     lib = L.lib()

@@ -103,6 +103,11 @@ def parse():
                          "(default 2048; 256 with --train)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this size (for counter calibration)")
+    ap.add_argument("--load-log", default="",
+                    help="after the timed region, run the workload's balancing loop (its "
+                         "step count, fresh seeded tokens each step; 50 for v3-skew-loop) and "
+                         "write one JSON line of load statistics per step to this file "
+                         "('-' for stderr)")
     return ap.parse_args()
 
 
@@ -205,7 +210,11 @@ def main():
     # activations read and written once)
     up_w = touched * 2 * w.I * w.H * es
     up_scales = touched * (2 * w.I // 128) * (w.H // 128) * 4 if w.expert == "e4m3" else 0
-    up_act = R * w.H * es + R * w.I * es + (R * (w.H // 128 + w.I // 128) * 4 if es == 1 else 0)
+    # activations: the dispatched rows (materialised: R rows of x_sorted; gathered: each
+    # token's row once, its other reads hit the L2) and h written once
+    x_rows = w.T if not args.materialize else R
+    up_act = (x_rows * w.H * es + R * w.I * es +
+              ((x_rows * (w.H // 128) + R * (w.I // 128)) * 4 if es == 1 else 0))
     up_bytes = up_w + up_scales + up_act
     if args.train:  # the gate/up pre-activations kept for the backward
         up_bytes += R * 2 * w.I * act_es
@@ -305,6 +314,9 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
 
+    if args.load_log:
+        load_log(args, w, layer, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         ffn_rows = args.cpu_ffn_rows or (256 if args.train else 2048)
@@ -328,6 +340,43 @@ def main():
         "experts_touched": touched,
     }
     print(json.dumps(out), flush=True)
+
+
+def load_log(args, w, layer, dev):
+    """The balancing loop with per-step load statistics (untimed): step s routes fresh
+    seeded tokens (seed x + s) with the bias left by step s-1, then updates the bias.
+    The statistics come from moe_seq_load_stats over the batch as one sequence (max,
+    min, experts without tokens, max/mean), the bias range from the bias itself."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from mixture_experts_layer_added_amd import _lib as L
+
+    out = sys.stderr if args.load_log == "-" else open(args.load_log, "w")
+    off = torch.tensor([0, w.T], dtype=torch.int32, device=dev)
+    c = torch.empty((1, w.E), dtype=torch.int32, device=dev)
+    st = torch.empty((1, 3), dtype=torch.int32, device=dev)
+    r = torch.empty((1,), dtype=torch.float32, device=dev)
+    b0 = layer.bias.clone()
+    layer.bias.copy_(workloads.make_router(w, dev)[1])  # the loop starts from the initial bias
+    for step in range(max(w.steps, 1)):
+        x = workloads.make_x(w, step=step, device=dev)
+        layer.forward(x)
+        L.moe_seq_load_stats(layer.p, layer.topk_idx, off, 1, c, st, r)
+        layer.bias_step(w.gamma)
+        s3 = st.cpu().numpy()[0]
+        b = layer.bias.cpu().numpy()
+        counts = np.sort(c.cpu().numpy()[0])[::-1]
+        out.write(json.dumps({"step": step, "max_over_mean": round(float(r.item()), 4),
+                              "max_load": int(s3[0]), "min_load": int(s3[1]),
+                              "zero_load_experts": int(s3[2]),
+                              "top16_share": round(float(counts[:16].sum() / counts.sum()), 4),
+                              "bias_min": float(b.min()), "bias_max": float(b.max())}) + "\n")
+    out.flush()
+    if out is not sys.stderr:
+        out.close()
+    layer.bias.copy_(b0)
 
 
 def route_only(args, w, dev):

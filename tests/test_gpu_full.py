@@ -164,30 +164,67 @@ def test_full_shape_forward(name, n_tok, gather):
     torch.cuda.empty_cache()
 
 
-def test_skew_loop_bias_trajectory():
+def _load_stats(layer, w):
+    """Batch load statistics of the last routing from the GPU: moe_seq_load_stats with
+    the batch as one sequence (max, min, experts without tokens, max/mean)."""
+    from mixture_experts_layer_added_amd import _lib as L
+    dev = layer.counts.device
+    off = torch.tensor([0, w.T], dtype=torch.int32, device=dev)
+    c = torch.empty((1, w.E), dtype=torch.int32, device=dev)
+    st = torch.empty((1, 3), dtype=torch.int32, device=dev)
+    r = torch.empty((1,), dtype=torch.float32, device=dev)
+    L.moe_seq_load_stats(layer.p, layer.topk_idx, off, 1, c, st, r)
+    return c, st, r
+
+
+def test_skew_loop_bias_trajectory(tmp_path):
     """50 forward + bias-update steps on fresh seeded x with Zipf-skewed router logits:
-    the GPU and oracle biases agree bit for bit after every step."""
+    the GPU and oracle biases agree bit for bit after every step.  Each step also logs
+    one JSON line of load statistics (max/mean, min, experts without tokens, bias range;
+    the pages follow expert utilisation as training goes, mpbf.cn section 6.2), taken on
+    the GPU and equal to the oracle's.  Then the run is resumed from a checkpoint: the
+    bias bits after step 25 are saved to a file, restored into the layer, and steps 25..49
+    repeated must end at the same bias bit for bit."""
+    import json
     w = workloads.get("v3-skew-loop")
     log(f"[skew loop] T={w.T}, {w.steps} steps, gamma={w.gamma}")
     layer, _ = build(w)
     wr = np_(layer.w_router)
     b_ref = np_(layer.bias).copy()
     ratios = []
+    half = w.steps // 2
+    ckpt = tmp_path / "bias_state.json"
     for step in range(w.steps):
         x = workloads.make_x(w, step=step, device="cuda")
         layer.step(x, w.gamma)
         _, _, counts, _ = oracle.route(np_(x), wr, b_ref, w.G, w.M, w.K, w.J)
         b_ref = oracle.bias_update(counts, w.T, w.K, w.gamma, b_ref)
+        c, st, r = _load_stats(layer, w)
         torch.cuda.synchronize()
         assert np.array_equal(np_(layer.counts), counts), step
         assert np.array_equal(np_(layer.bias).view(np.uint32), b_ref.view(np.uint32)), step
-        ratios.append(counts.max() / (w.T * w.K / w.E))
-        if step % 10 == 0 or step == w.steps - 1:
-            log(f"    step {step:2d}: max/mean load {ratios[-1]:.3f}, top-16 share "
-                f"{workloads.zipf_top16_share(counts):.3f}, bias range "
-                f"[{b_ref.min():+.2f}, {b_ref.max():+.2f}]")
-    log("    max/mean per step: " + " ".join(f"{r:.2f}" for r in ratios))
+        rc, rs, rr = oracle.seq_load_stats(np_(layer.topk_idx), w.E, [0, w.T])
+        assert np.array_equal(np_(c), rc) and np.array_equal(np_(st), rs), step
+        assert np_(r).view(np.uint32)[0] == rr.view(np.uint32)[0], step
+        ratios.append(float(rr[0]))
+        log(json.dumps({"step": step, "max_over_mean": round(float(rr[0]), 4),
+                        "max_load": int(rs[0, 0]), "min_load": int(rs[0, 1]),
+                        "zero_load_experts": int(rs[0, 2]),
+                        "top16_share": round(workloads.zipf_top16_share(counts), 4),
+                        "bias_min": float(b_ref.min()), "bias_max": float(b_ref.max())}))
+        if step == half - 1:
+            ckpt.write_text(json.dumps({"step": half,
+                                        "bias_bits": np_(layer.bias).view(np.uint32).tolist()}))
+    b_final = np_(layer.bias).copy()
     # the balancing pushes the load toward uniform (the pages describe this qualitatively)
     assert ratios[-1] < ratios[0]
+    # resume from the checkpoint
+    state = json.loads(ckpt.read_text())
+    layer.bias.copy_(torch.from_numpy(np.array(state["bias_bits"], np.uint32).view(np.float32)))
+    for step in range(state["step"], w.steps):
+        layer.step(workloads.make_x(w, step=step, device="cuda"), w.gamma)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(layer.bias).view(np.uint32), b_final.view(np.uint32))
+    log(f"    resumed from step {state['step']}: final bias bit-identical to the straight run")
     del layer
     torch.cuda.empty_cache()

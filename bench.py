@@ -291,7 +291,13 @@ def main():
                     "bytes_per_launch": bw_bytes // 2, "ms_per_launch": round(per_launch_ms, 4),
                     "traffic": None}
     else:
+        # the bound is the roof the call's arithmetic intensity meets first: HBM below the
+        # ridge (peak flop/s over peak bytes/s), the matrix cores above it (a large batch
+        # puts enough rows on every expert)
         up_gbs = gbs(up_bytes, avg_ms["ffn_up"])
+        up_tfs = tfs(up_flops, avg_ms["ffn_up"])
+        intensity = up_flops / up_bytes
+        ridge = MFMA_PEAK[w.expert] * 1e12 / (HBM_PEAK_GBS * 1e9)
         roofline = {"kernel": "gate/up GEMM + SwiGLU call: k_gemm_bf16<true> (routed experts, "
                               "grouped) + k_gemm_dense_swiglu_bf16 (the shared expert, when T >= "
                               "2048)" if w.expert == "bf16" else
@@ -300,9 +306,17 @@ def main():
                     "bound": "hbm", "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(up_gbs / HBM_PEAK_GBS, 4),
                     "bytes_per_launch": up_bytes, "ms_per_launch": round(avg_ms["ffn_up"], 4),
-                    "traffic": None}
+                    "traffic": None, "intensity_flop_per_byte": round(intensity, 1),
+                    "ridge_flop_per_byte": round(ridge, 1)}
+        if intensity >= ridge:
+            roofline.update({"bound": "mfma", "achieved": round(up_tfs, 1),
+                             "peak": MFMA_PEAK[w.expert], "unit": "TFLOP/s",
+                             "frac": round(up_tfs / MFMA_PEAK[w.expert], 4),
+                             "flops_per_launch": up_flops})
     dispatch = "materialized x_sorted" if args.materialize else "gather from x"
     traffic, src = measured_traffic(w.name, w.expert, dispatch, args.train)
+    if args.tokens and args.tokens != workloads.get(w.name).T:
+        traffic, src = None, f"counters were taken at T={workloads.get(w.name).T}"
     roofline["traffic"] = traffic
     roofline["traffic_source"] = src
     roofline["kernel_source_sha256"] = kernel_source_sha(w.expert, args.train)

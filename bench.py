@@ -44,14 +44,17 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha(expert, train=False):
+def kernel_source_sha(expert, train=False, packed=False):
     """sha256 over the sources that define the measured kernel: the gate/up GEMM of this
-    expert dtype, or (train) the weight-gradient GEMM."""
+    expert dtype (bf16: over packed or natural-layout weights), or (train) the
+    weight-gradient GEMM."""
     csrc = os.path.join(ROOT, "mixture_experts_layer_added_amd", "csrc")
     if train:
         files = ["gemm_bwd.hip", "common.h"]
     elif expert == "e4m3":
         files = ["gemm_fp8.hip", "gemm_dense.hip", "common.h"]
+    elif packed:
+        files = ["gemm_packed.hip", "gemm_dense.hip", "common.h"]
     else:
         files = ["gemm.hip", "gemm_dense.hip", "common.h"]
     h = hashlib.sha256()
@@ -61,7 +64,7 @@ def kernel_source_sha(expert, train=False):
     return h.hexdigest()
 
 
-def measured_traffic(workload, expert, dispatch, train=False):
+def measured_traffic(workload, expert, dispatch, train=False, packed=False):
     """HBM bytes per launch of the measured kernel (gate/up GEMM, or with train the
     weight-gradient GEMM) from the committed FETCH_SIZE / WRITE_SIZE counter summary of
     this workload, or None when there is none or the kernel source has changed since
@@ -75,7 +78,7 @@ def measured_traffic(workload, expert, dispatch, train=False):
     if not m:
         return None, "counter summary unreadable"
     rec = json.loads(m.group(1))
-    if rec.get("source_sha256") != kernel_source_sha(expert, train):
+    if rec.get("source_sha256") != kernel_source_sha(expert, train, packed):
         return None, "kernel changed since the counters were taken"
     if rec.get("dispatch") != dispatch:
         return None, f"counters were taken with dispatch '{rec.get('dispatch')}'"
@@ -96,6 +99,9 @@ def parse():
     ap.add_argument("--route-only", action="store_true",
                     help="time moe_route alone (router logits + group-limited top-K); with "
                          "--tokens it runs at batch sizes whose expert FFN buffers would not fit")
+    ap.add_argument("--natural", action="store_true",
+                    help="bf16: run the expert GEMMs over the natural weight layout (the LDS-ring "
+                         "kernels) instead of the packed layout")
     ap.add_argument("--train", action="store_true",
                     help="time forward + bias update + backward (bf16 / fp32 experts)")
     ap.add_argument("--cpu-ffn-rows", type=int, default=0,
@@ -154,7 +160,8 @@ def main():
     if args.train and w.expert == "e4m3":
         raise SystemExit("--train: the backward is built for the bf16 and fp32 expert paths")
     layer = MoELayer(shape, w_router, bias, w13, w2, s13, s2, device=dev,
-                     gather=not args.materialize, train=args.train)
+                     gather=not args.materialize, train=args.train,
+                     packed=False if args.natural else None)
     dy = workloads.make_dy(w, device=dev) if args.train else None
     stream = torch.cuda.current_stream()
 
@@ -298,7 +305,8 @@ def main():
         up_tfs = tfs(up_flops, avg_ms["ffn_up"])
         intensity = up_flops / up_bytes
         ridge = MFMA_PEAK[w.expert] * 1e12 / (HBM_PEAK_GBS * 1e9)
-        roofline = {"kernel": "gate/up GEMM + SwiGLU call: k_gemm_bf16<true> (routed experts, "
+        gk = "k_gemm_packed<true>" if layer.packed else "k_gemm_bf16<true>"
+        roofline = {"kernel": f"gate/up GEMM + SwiGLU call: {gk} (routed experts, "
                               "grouped) + k_gemm_dense_swiglu_bf16 (the shared expert, when T >= "
                               "2048)" if w.expert == "bf16" else
                     "gate/up GEMM + SwiGLU call (e4m3): k_gemm_fp8<true> (routed experts, grouped) "
@@ -314,12 +322,12 @@ def main():
                              "frac": round(up_tfs / MFMA_PEAK[w.expert], 4),
                              "flops_per_launch": up_flops})
     dispatch = "materialized x_sorted" if args.materialize else "gather from x"
-    traffic, src = measured_traffic(w.name, w.expert, dispatch, args.train)
+    traffic, src = measured_traffic(w.name, w.expert, dispatch, args.train, layer.packed)
     if args.tokens and args.tokens != workloads.get(w.name).T:
         traffic, src = None, f"counters were taken at T={workloads.get(w.name).T}"
     roofline["traffic"] = traffic
     roofline["traffic_source"] = src
-    roofline["kernel_source_sha256"] = kernel_source_sha(w.expert, args.train)
+    roofline["kernel_source_sha256"] = kernel_source_sha(w.expert, args.train, layer.packed)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20)
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -345,7 +353,9 @@ def main():
         "dtype": w.expert, "data": "synthetic (seeded; weights N(0,0.006), x N(0,1))",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "G": w.G, "M": w.M,
                    "K": w.K, "J": w.J, "I": w.I, "S": w.S, "act": w.act, "expert": w.expert,
-                   "dispatch": dispatch, "step": "forward + bias update + backward"
+                   "dispatch": dispatch,
+                   "weights": "packed" if layer.packed else "natural layout",
+                   "step": "forward + bias update + backward"
                    if args.train else "forward + bias update",
                    "parallelism": "single GPU"},
         "roofline": roofline,

@@ -23,7 +23,8 @@ EXPORTS = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_up",
            "moe_status_str", "moe_last_error", "moe_expert_ffn_up_save", "moe_combine_backward",
            "moe_router_backward", "moe_expert_ffn_backward_input",
            "moe_expert_ffn_backward_weight", "moe_unpermute_sum", "moe_permute_noalloc",
-           "moe_seq_load_stats")
+           "moe_seq_load_stats", "moe_pack_expert_weights", "moe_expert_ffn_up_packed",
+           "moe_expert_ffn_down_packed")
 
 
 class MoeError(RuntimeError):
@@ -72,6 +73,9 @@ def lib():
         L.moe_expert_ffn_backward_weight.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_unpermute_sum.argtypes = [pp, vp, vp, vp, vp, vp]
         L.moe_expert_ffn_down.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_pack_expert_weights.argtypes = [pp, vp, vp, vp, vp, vp]
+        L.moe_expert_ffn_up_packed.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_expert_ffn_down_packed.argtypes = [pp, vp, vp, vp, vp, vp]
         L.moe_combine.argtypes = [pp, vp, vp, vp, vp, vp]
         L.moe_bias_update.argtypes = [pp, vp, f32, vp, vp]
         L.moe_quantize_weights_fp8.argtypes = [vp, vp, vp, i64, i32, i32, vp]
@@ -86,7 +90,9 @@ def lib():
                   "moe_combine", "moe_bias_update", "moe_quantize_weights_fp8",
                   "moe_expert_ffn_up_save", "moe_combine_backward", "moe_router_backward",
                   "moe_expert_ffn_backward_input", "moe_expert_ffn_backward_weight",
-                  "moe_unpermute_sum", "moe_permute_noalloc", "moe_seq_load_stats"):
+                  "moe_unpermute_sum", "moe_permute_noalloc", "moe_seq_load_stats",
+                  "moe_pack_expert_weights", "moe_expert_ffn_up_packed",
+                  "moe_expert_ffn_down_packed"):
             getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -204,6 +210,25 @@ def moe_quantize_weights_fp8(w_bf16, w_fp8, scale, batch, rows, cols, stream=Non
     _check(lib().moe_quantize_weights_fp8(_ptr(w_bf16), _ptr(w_fp8), _ptr(scale), batch, rows,
                                           cols, _stream(stream)), "moe_quantize_weights_fp8")
 
+
+
+def moe_pack_expert_weights(p, w13, w2, w13_packed, w2_packed, stream=None):
+    _check(lib().moe_pack_expert_weights(ctypes.byref(p), _ptr(w13), _ptr(w2), _ptr(w13_packed),
+                                         _ptr(w2_packed), _stream(stream)),
+           "moe_pack_expert_weights")
+
+
+def moe_expert_ffn_up_packed(p, x, sorted_token, offsets, w13, w13_packed, h, au=None,
+                             stream=None):
+    _check(lib().moe_expert_ffn_up_packed(ctypes.byref(p), _ptr(x), _ptr(sorted_token),
+                                          _ptr(offsets), _ptr(w13), _ptr(w13_packed), _ptr(h),
+                                          _ptr(au), _stream(stream)), "moe_expert_ffn_up_packed")
+
+
+def moe_expert_ffn_down_packed(p, h, offsets, w2_packed, y_sorted, stream=None):
+    _check(lib().moe_expert_ffn_down_packed(ctypes.byref(p), _ptr(h), _ptr(offsets),
+                                            _ptr(w2_packed), _ptr(y_sorted), _stream(stream)),
+           "moe_expert_ffn_down_packed")
 
 
 def moe_expert_ffn_up_save(p, x, sorted_token, offsets, w13, h, au, stream=None):

@@ -504,6 +504,67 @@ moe_status moe_expert_ffn_backward_weight(const moe_problem* p, const void* x,
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn_backward_weight launch");
 }
 
+static moe_status require_packed(const Dims& d, const char* call) {
+  if (!packed_supported(d))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: packed weights are built for act and expert dtype BF16",
+                call);
+  return MOE_OK;
+}
+
+moe_status moe_pack_expert_weights(const moe_problem* p, const void* w13, const void* w2,
+                                   void* w13_packed, void* w2_packed, void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  if ((s = require_packed(d, "moe_pack_expert_weights")) != MOE_OK) return s;
+  if (!w13 && !w2) return fail(MOE_ERR_INVALID_ARG, "w13 and w2 are both NULL");
+  if ((w13 && !w13_packed) || (w2 && !w2_packed))
+    return fail(MOE_ERR_INVALID_ARG, "a packed output is NULL for a given input");
+  if ((w13 && w13 == w13_packed) || (w2 && w2 == w2_packed))
+    return fail(MOE_ERR_INVALID_ARG, "packing cannot run in place");
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  hipError_t e = launch_pack_weights(d, w13, w2, w13_packed, w2_packed,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_pack_expert_weights launch");
+}
+
+moe_status moe_expert_ffn_up_packed(const moe_problem* p, const void* x,
+                                    const int32_t* sorted_token, const int32_t* offsets,
+                                    const void* w13, const void* w13_packed, void* h, void* au,
+                                    void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  if ((s = require_packed(d, "moe_expert_ffn_up_packed")) != MOE_OK) return s;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w13);
+  REQUIRE_PTR(w13_packed);
+  REQUIRE_PTR(h);
+  if (!offsets) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL");
+  if (sorted_token && d.T * (int64_t)d.H * 2 >= ((int64_t)1 << 31) - 16)
+    return fail(MOE_ERR_INVALID_ARG, "T*H*2 must be < 2^31 - 16 (32-bit row offsets)");
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  hipError_t e = launch_ffn_up_packed(d, x, offsets, sorted_token, w13, w13_packed, h, au,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn_up_packed launch");
+}
+
+moe_status moe_expert_ffn_down_packed(const moe_problem* p, const void* h, const int32_t* offsets,
+                                      const void* w2_packed, void* y_sorted, void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  if ((s = require_packed(d, "moe_expert_ffn_down_packed")) != MOE_OK) return s;
+  REQUIRE_PTR(h);
+  REQUIRE_PTR(w2_packed);
+  REQUIRE_PTR(y_sorted);
+  if (!offsets) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL");
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  hipError_t e = launch_ffn_down_packed(d, h, offsets, w2_packed, y_sorted,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn_down_packed launch");
+}
+
 moe_status moe_quantize_weights_fp8(const void* w_bf16, void* w_fp8, float* scale,
                                     int64_t batch, int32_t rows, int32_t cols, void* stream) {
   if (batch < 1 || rows < 128 || cols < 128 || rows % 128 || cols % 128)

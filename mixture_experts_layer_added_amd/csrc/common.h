@@ -223,6 +223,20 @@ hipError_t launch_fp8_down(const Dims& d, const void* h, const float* h_scale,
                            const int32_t* offsets, const void* w2, const float* w2_scale, void* ys,
                            hipStream_t st);
 
+// bf16 expert GEMMs over packed weights (gemm_packed.hip): the layout, its sizes
+// (elements, equal to the natural layout's) and the pack; the gate/up launch takes the
+// natural w13 as well, for the shared expert's dense launch (dense_shared)
+bool packed_supported(const Dims& d);
+size_t packed_w13_elems(const Dims& d);
+size_t packed_w2_elems(const Dims& d);
+hipError_t launch_pack_weights(const Dims& d, const void* w13, const void* w2, void* p13,
+                               void* p2, hipStream_t st);
+hipError_t launch_ffn_up_packed(const Dims& d, const void* xs, const int32_t* offsets,
+                                const int32_t* gather, const void* w13, const void* p13, void* h,
+                                void* au, hipStream_t st);
+hipError_t launch_ffn_down_packed(const Dims& d, const void* h, const int32_t* offsets,
+                                  const void* p2, void* ys, hipStream_t st);
+
 hipError_t launch_combine(const Dims& d, const void* ys, const int32_t* inv_perm,
                           const float* gate, void* y, hipStream_t st);
 

@@ -60,18 +60,27 @@ class MoELayer:
     results are identical and the permuted copy of x is never written.
     train=True (bf16 / fp32): the gate/up GEMM also keeps the pre-activations (au) and
     backward(dy) computes dx, dw_router, dw13 and dw2 (weight gradients in fp32).
+    packed (bf16 experts; default on there): the expert GEMMs run over copies of w13 and
+    w2 in the library's packed layout, made once here (same results, bit for bit).
     """
 
     def __init__(self, shape: Shape, w_router, bias, w13, w2, w13_scale=None, w2_scale=None,
-                 device="cuda", gather=False, train=False):
+                 device="cuda", gather=False, train=False, packed=None):
         self.shape = shape
         self.gather = gather
         self.train = train
+        bf16 = shape.expert == "bf16" and shape.act == "bf16"
+        self.packed = bf16 if packed is None else bool(packed)
+        assert bf16 or not self.packed, "packed weights are built for the bf16 path"
         self._x = None
         self._xin = None
         self.p = shape.problem()
         self.w_router, self.bias = w_router, bias
         self.w13, self.w2, self.w13_scale, self.w2_scale = w13, w2, w13_scale, w2_scale
+        self.w13p = self.w2p = None
+        if self.packed:
+            self.w13p, self.w2p = torch.empty_like(w13), torch.empty_like(w2)
+            L.moe_pack_expert_weights(self.p, w13, w2, self.w13p, self.w2p)
         T, H, E, K, R = shape.T, shape.H, shape.E, shape.K, shape.R
         act = torch.float32 if shape.act == "f32" else torch.bfloat16
         dev = torch.device(device)
@@ -144,7 +153,11 @@ class MoELayer:
             self._xin = x
 
     def expert_ffn_up(self, stream=None):
-        if self.train:
+        if self.packed:
+            xin, st = (self._x, self.sorted_token) if self.gather else (self.x_sorted, None)
+            L.moe_expert_ffn_up_packed(self.p, xin, st, self.offsets, self.w13, self.w13p,
+                                       self.h, self.au if self.train else None, stream)
+        elif self.train:
             xin, st = (self._x, self.sorted_token) if self.gather else (self.x_sorted, None)
             L.moe_expert_ffn_up_save(self.p, xin, st, self.offsets, self.w13, self.h, self.au,
                                      stream)
@@ -158,6 +171,10 @@ class MoELayer:
                                 self.w13_scale, self.h, self.h_scale, stream)
 
     def expert_ffn_down(self, stream=None):
+        if self.packed:
+            L.moe_expert_ffn_down_packed(self.p, self.h, self.offsets, self.w2p, self.y_sorted,
+                                         stream)
+            return
         L.moe_expert_ffn_down(self.p, self.h, self.h_scale, self.offsets, self.w2, self.w2_scale,
                               self.y_sorted, stream)
 

@@ -44,11 +44,11 @@ def run_oracle_route(w, inp):
                         want_logits=True)
 
 
-def gpu_layer(w, inp, w13=None, w2=None, s13=None, s2=None):
+def gpu_layer(w, inp, w13=None, w2=None, s13=None, s2=None, packed=None):
     from mixture_experts_layer_added_amd.layer import MoELayer
     return MoELayer(shape_of(w), to_dev(inp["w_router"]), to_dev(inp["bias"]),
                     to_dev(inp["w13"]) if w13 is None else w13,
-                    to_dev(inp["w2"]) if w2 is None else w2, s13, s2)
+                    to_dev(inp["w2"]) if w2 is None else w2, s13, s2, packed=packed)
 
 
 def fp8_weights(inp):
@@ -113,9 +113,14 @@ def test_quantize_weights_bitexact(name):
     assert np.array_equal(np_(q2), o2) and np.array_equal(np_(s2).view(np.uint32), os2.view(np.uint32))
 
 
-@pytest.mark.parametrize("name", CASES)
-def test_expert_ffn_tolerance(name):
-    log(f"[expert_ffn] {name}")
+FFN_CASES = [(n, None) for n in CASES] + [(n, False) for n in CASES if n.endswith("-bf16")]
+
+
+@pytest.mark.parametrize("name,packed", FFN_CASES)
+def test_expert_ffn_tolerance(name, packed):
+    """bf16 cases run twice: over packed weights (the default) and over the natural
+    layout (the LDS-ring kernels)."""
+    log(f"[expert_ffn] {name} packed={packed}")
     w = case(name)
     inp = make_cpu_inputs(w)
     idx, gate, counts, _ = run_oracle_route(w, inp)
@@ -130,7 +135,7 @@ def test_expert_ffn_tolerance(name):
                           torch.from_numpy(s13).cuda(), torch.from_numpy(s2).cuda())
         layer.x_scale.copy_(torch.from_numpy(xsc))
     else:
-        layer = gpu_layer(w, inp)
+        layer = gpu_layer(w, inp, packed=packed)
         w13n, w2n = np_(inp["w13"]), np_(inp["w2"])
     for g in range(w.E + w.S):
         lo, hi = int(off[g]), int(off[g + 1])

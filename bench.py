@@ -101,7 +101,9 @@ def parse():
                          "--tokens it runs at batch sizes whose expert FFN buffers would not fit")
     ap.add_argument("--natural", action="store_true",
                     help="bf16: run the expert GEMMs over the natural weight layout (the LDS-ring "
-                         "kernels) instead of the packed layout")
+                         "kernels); default: packed up to 160 rows per expert on average")
+    ap.add_argument("--packed", action="store_true",
+                    help="bf16: run the expert GEMMs over packed weights at any batch size")
     ap.add_argument("--train", action="store_true",
                     help="time forward + bias update + backward (bf16 / fp32 experts)")
     ap.add_argument("--cpu-ffn-rows", type=int, default=0,
@@ -161,7 +163,7 @@ def main():
         raise SystemExit("--train: the backward is built for the bf16 and fp32 expert paths")
     layer = MoELayer(shape, w_router, bias, w13, w2, s13, s2, device=dev,
                      gather=not args.materialize, train=args.train,
-                     packed=False if args.natural else None)
+                     packed=False if args.natural else (True if args.packed else None))
     dy = workloads.make_dy(w, device=dev) if args.train else None
     stream = torch.cuda.current_stream()
 

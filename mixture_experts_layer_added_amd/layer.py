@@ -47,6 +47,10 @@ def quantize_weights_fp8(w: torch.Tensor, stream=None):
     return q, s
 
 
+# batches up to this mean load per routed expert use the packed-weight GEMMs by default
+PACKED_MAX_MEAN_ROWS = 160
+
+
 class MoELayer:
     """Buffers for one batch of T tokens.
 
@@ -60,8 +64,11 @@ class MoELayer:
     results are identical and the permuted copy of x is never written.
     train=True (bf16 / fp32): the gate/up GEMM also keeps the pre-activations (au) and
     backward(dy) computes dx, dw_router, dw13 and dw2 (weight gradients in fp32).
-    packed (bf16 experts; default on there): the expert GEMMs run over copies of w13 and
-    w2 in the library's packed layout, made once here (same results, bit for bit).
+    packed (bf16 experts): the expert GEMMs run over copies of w13 and w2 in the library's
+    packed layout, made once here (same results, bit for bit).  Default: on when the
+    mean load per routed expert, T*K/E, is at most PACKED_MAX_MEAN_ROWS -- the packed
+    kernels take at most 192 rows of an expert per tile (a larger expert streams its
+    weights once per tile), the natural-layout kernels 256.
     """
 
     def __init__(self, shape: Shape, w_router, bias, w13, w2, w13_scale=None, w2_scale=None,
@@ -70,7 +77,9 @@ class MoELayer:
         self.gather = gather
         self.train = train
         bf16 = shape.expert == "bf16" and shape.act == "bf16"
-        self.packed = bf16 if packed is None else bool(packed)
+        if packed is None:
+            packed = bf16 and shape.T * shape.K <= PACKED_MAX_MEAN_ROWS * shape.E
+        self.packed = bool(packed)
         assert bf16 or not self.packed, "packed weights are built for the bf16 path"
         self._x = None
         self._xin = None

@@ -113,13 +113,14 @@ def test_quantize_weights_bitexact(name):
     assert np.array_equal(np_(q2), o2) and np.array_equal(np_(s2).view(np.uint32), os2.view(np.uint32))
 
 
-FFN_CASES = [(n, None) for n in CASES] + [(n, False) for n in CASES if n.endswith("-bf16")]
+FFN_CASES = ([(n, None) for n in CASES if not n.endswith("-bf16")] +
+             [(n, pk) for n in CASES if n.endswith("-bf16") for pk in (True, False)])
 
 
 @pytest.mark.parametrize("name,packed", FFN_CASES)
 def test_expert_ffn_tolerance(name, packed):
-    """bf16 cases run twice: over packed weights (the default) and over the natural
-    layout (the LDS-ring kernels)."""
+    """bf16 cases run twice: over packed weights and over the natural layout (the
+    LDS-ring kernels)."""
     log(f"[expert_ffn] {name} packed={packed}")
     w = case(name)
     inp = make_cpu_inputs(w)

@@ -209,39 +209,46 @@ moe_status moe_expert_ffn_down(const moe_problem* p, const void* h, const float*
                                void* y_sorted, void* stream);
 
 /* The expert FFN of moe_expert_ffn_up(_gather, _save) and moe_expert_ffn_down (same
- * passages, same results bit for bit) over expert weights in a pre-arranged layout that
- * lets the GEMMs stream each weight byte straight into the matrix-core operands.
- * BF16 act and expert dtypes only (else MOE_ERR_UNSUPPORTED).
+ * passages, same arithmetic) over expert weights in a pre-arranged layout that lets the
+ * GEMMs stream each weight byte straight into the matrix-core operands.  act dtype BF16
+ * with expert dtype BF16 or FP8_E4M3 (else MOE_ERR_UNSUPPORTED).  BF16 results equal the
+ * natural-layout calls bit for bit; FP8 results follow the same block-scaled promotion.
  *
- * moe_pack_expert_weights: w13 [E+S, 2I, H] and w2 [E+S, H, I] bf16 (natural layout, as
- * above) -> w13_packed and w2_packed, each the same number of bytes as its input.  The
- * packed layout (per group, blocks of 64 weight rows, 64-deep k steps per block, 8 x 64
- * chunks of 16 bytes per step) is private to this library: its only consumers are the
- * two calls below.  Either pair may be NULL (that matrix is not packed); the call must
- * not be in place.  Offline preparation, like moe_quantize_weights_fp8. */
+ * moe_pack_expert_weights: w13 [E+S, 2I, H] and w2 [E+S, H, I] in the expert dtype
+ * (natural layout as above; FP8: the E4M3 codes of moe_quantize_weights_fp8) ->
+ * w13_packed and w2_packed, each the same number of bytes as its input.  The packed
+ * layout (per group, blocks of 64 weight rows, 64-deep (BF16) or 128-deep (FP8) k steps
+ * per block, 8 x 64 chunks of 16 bytes per step) is private to this library: its only
+ * consumers are the two calls below.  The FP8 weight scales are not packed.  Either pair
+ * may be NULL (that matrix is not packed); the call must not be in place.  Offline
+ * preparation, like moe_quantize_weights_fp8. */
 moe_status moe_pack_expert_weights(const moe_problem* p, const void* w13, const void* w2,
                                    void* w13_packed, void* w2_packed, void* stream);
 
 /* Gate/up GEMM + SwiGLU over packed weights.
  *   x            sorted_token == NULL: x_sorted [R,H] (moe_permute); else x [T,H] and row r
  *                of the permuted order is x[sorted_token[r]] (limit as
- *                moe_expert_ffn_up_gather)
+ *                moe_expert_ffn_up_gather); FP8: E4M3 codes
+ *   x_scale      FP8: [R,H/128] or [T,H/128] fp32 (as x), else NULL
  *   offsets      from moe_permute
  *   w13          natural layout (the shared expert's rows are multiplied by a dense
  *                kernel that reads it when T >= 2048)
- *   w13_packed   from moe_pack_expert_weights
- *   h  [R,I] bf16 out;  au [R,2I] bf16 out or NULL (the pre-activations, as
- *   moe_expert_ffn_up_save). */
-moe_status moe_expert_ffn_up_packed(const moe_problem* p, const void* x,
+ *   w13_packed   from moe_pack_expert_weights;  w13_scale  FP8 only, as moe_expert_ffn
+ *   h  [R,I] out (bf16, or E4M3 codes with h_scale [R,I/128] fp32 out, as
+ *   moe_expert_ffn_up);  au [R,2I] bf16 out or NULL (the pre-activations, as
+ *   moe_expert_ffn_up_save; bf16 only). */
+moe_status moe_expert_ffn_up_packed(const moe_problem* p, const void* x, const float* x_scale,
                                     const int32_t* sorted_token, const int32_t* offsets,
-                                    const void* w13, const void* w13_packed, void* h, void* au,
+                                    const void* w13, const void* w13_packed,
+                                    const float* w13_scale, void* h, float* h_scale, void* au,
                                     void* stream);
 
 /* Down GEMM over packed weights: y_sorted [R,H] bf16 out = h W2[g]^T per group
- * (h [R,I] from moe_expert_ffn_up_packed or moe_expert_ffn_up; w2_packed from
- * moe_pack_expert_weights). */
-moe_status moe_expert_ffn_down_packed(const moe_problem* p, const void* h, const int32_t* offsets,
-                                      const void* w2_packed, void* y_sorted, void* stream);
+ * (h, h_scale from moe_expert_ffn_up_packed or moe_expert_ffn_up; w2_packed from
+ * moe_pack_expert_weights; w2_scale FP8 only, as moe_expert_ffn). */
+moe_status moe_expert_ffn_down_packed(const moe_problem* p, const void* h, const float* h_scale,
+                                      const int32_t* offsets, const void* w2_packed,
+                                      const float* w2_scale, void* y_sorted, void* stream);
 
 /* Combine (blog.resmic.cn section 核心架构二: shared output + gate-weighted routed
  * outputs):  acc = 0; for k = 0..K-1: acc = fma(gate[t,k], Y[inv_perm[t,k]], acc);

@@ -74,8 +74,8 @@ def lib():
         L.moe_unpermute_sum.argtypes = [pp, vp, vp, vp, vp, vp]
         L.moe_expert_ffn_down.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_pack_expert_weights.argtypes = [pp, vp, vp, vp, vp, vp]
-        L.moe_expert_ffn_up_packed.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
-        L.moe_expert_ffn_down_packed.argtypes = [pp, vp, vp, vp, vp, vp]
+        L.moe_expert_ffn_up_packed.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_expert_ffn_down_packed.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_combine.argtypes = [pp, vp, vp, vp, vp, vp]
         L.moe_bias_update.argtypes = [pp, vp, f32, vp, vp]
         L.moe_quantize_weights_fp8.argtypes = [vp, vp, vp, i64, i32, i32, vp]
@@ -218,16 +218,20 @@ def moe_pack_expert_weights(p, w13, w2, w13_packed, w2_packed, stream=None):
            "moe_pack_expert_weights")
 
 
-def moe_expert_ffn_up_packed(p, x, sorted_token, offsets, w13, w13_packed, h, au=None,
-                             stream=None):
-    _check(lib().moe_expert_ffn_up_packed(ctypes.byref(p), _ptr(x), _ptr(sorted_token),
-                                          _ptr(offsets), _ptr(w13), _ptr(w13_packed), _ptr(h),
-                                          _ptr(au), _stream(stream)), "moe_expert_ffn_up_packed")
+def moe_expert_ffn_up_packed(p, x, x_scale, sorted_token, offsets, w13, w13_packed, w13_scale,
+                             h, h_scale, au=None, stream=None):
+    _check(lib().moe_expert_ffn_up_packed(ctypes.byref(p), _ptr(x), _ptr(x_scale),
+                                          _ptr(sorted_token), _ptr(offsets), _ptr(w13),
+                                          _ptr(w13_packed), _ptr(w13_scale), _ptr(h),
+                                          _ptr(h_scale), _ptr(au), _stream(stream)),
+           "moe_expert_ffn_up_packed")
 
 
-def moe_expert_ffn_down_packed(p, h, offsets, w2_packed, y_sorted, stream=None):
-    _check(lib().moe_expert_ffn_down_packed(ctypes.byref(p), _ptr(h), _ptr(offsets),
-                                            _ptr(w2_packed), _ptr(y_sorted), _stream(stream)),
+def moe_expert_ffn_down_packed(p, h, h_scale, offsets, w2_packed, w2_scale, y_sorted,
+                               stream=None):
+    _check(lib().moe_expert_ffn_down_packed(ctypes.byref(p), _ptr(h), _ptr(h_scale),
+                                            _ptr(offsets), _ptr(w2_packed), _ptr(w2_scale),
+                                            _ptr(y_sorted), _stream(stream)),
            "moe_expert_ffn_down_packed")
 
 

@@ -506,7 +506,8 @@ moe_status moe_expert_ffn_backward_weight(const moe_problem* p, const void* x,
 
 static moe_status require_packed(const Dims& d, const char* call) {
   if (!packed_supported(d))
-    return fail(MOE_ERR_UNSUPPORTED, "%s: packed weights are built for act and expert dtype BF16",
+    return fail(MOE_ERR_UNSUPPORTED,
+                "%s: packed weights are built for act dtype BF16 with expert dtype BF16 or FP8",
                 call);
   return MOE_OK;
 }
@@ -523,14 +524,17 @@ moe_status moe_pack_expert_weights(const moe_problem* p, const void* w13, const 
   if ((w13 && w13 == w13_packed) || (w2 && w2 == w2_packed))
     return fail(MOE_ERR_INVALID_ARG, "packing cannot run in place");
   if ((s = check_device(nullptr)) != MOE_OK) return s;
-  hipError_t e = launch_pack_weights(d, w13, w2, w13_packed, w2_packed,
-                                     static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = d.expert == MOE_FP8_E4M3
+                     ? launch_pack_weights_fp8(d, w13, w2, w13_packed, w2_packed, st)
+                     : launch_pack_weights(d, w13, w2, w13_packed, w2_packed, st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_pack_expert_weights launch");
 }
 
-moe_status moe_expert_ffn_up_packed(const moe_problem* p, const void* x,
+moe_status moe_expert_ffn_up_packed(const moe_problem* p, const void* x, const float* x_scale,
                                     const int32_t* sorted_token, const int32_t* offsets,
-                                    const void* w13, const void* w13_packed, void* h, void* au,
+                                    const void* w13, const void* w13_packed,
+                                    const float* w13_scale, void* h, float* h_scale, void* au,
                                     void* stream) {
   Dims d;
   moe_status s = validate(p, &d);
@@ -541,16 +545,26 @@ moe_status moe_expert_ffn_up_packed(const moe_problem* p, const void* x,
   REQUIRE_PTR(w13_packed);
   REQUIRE_PTR(h);
   if (!offsets) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL");
-  if (sorted_token && d.T * (int64_t)d.H * 2 >= ((int64_t)1 << 31) - 16)
-    return fail(MOE_ERR_INVALID_ARG, "T*H*2 must be < 2^31 - 16 (32-bit row offsets)");
+  const bool fp8 = d.expert == MOE_FP8_E4M3;
+  if (fp8 && (!x_scale || !w13_scale || !h_scale))
+    return fail(MOE_ERR_INVALID_ARG, "the FP8 path needs x_scale, w13_scale, h_scale");
+  if (fp8 && au)
+    return fail(MOE_ERR_INVALID_ARG, "au (the pre-activations) is kept by the bf16 path only");
+  const int es = fp8 ? 1 : 2;
+  if (sorted_token && d.T * (int64_t)d.H * es >= ((int64_t)1 << 31) - 16)
+    return fail(MOE_ERR_INVALID_ARG, "T*H*%d must be < 2^31 - 16 (32-bit row offsets)", es);
   if ((s = check_device(nullptr)) != MOE_OK) return s;
-  hipError_t e = launch_ffn_up_packed(d, x, offsets, sorted_token, w13, w13_packed, h, au,
-                                      static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = fp8 ? launch_ffn_up_packed_fp8(d, x, x_scale, offsets, sorted_token, w13,
+                                                w13_packed, w13_scale, h, h_scale, st)
+                     : launch_ffn_up_packed(d, x, offsets, sorted_token, w13, w13_packed, h, au,
+                                            st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn_up_packed launch");
 }
 
-moe_status moe_expert_ffn_down_packed(const moe_problem* p, const void* h, const int32_t* offsets,
-                                      const void* w2_packed, void* y_sorted, void* stream) {
+moe_status moe_expert_ffn_down_packed(const moe_problem* p, const void* h, const float* h_scale,
+                                      const int32_t* offsets, const void* w2_packed,
+                                      const float* w2_scale, void* y_sorted, void* stream) {
   Dims d;
   moe_status s = validate(p, &d);
   if (s != MOE_OK) return s;
@@ -559,9 +573,14 @@ moe_status moe_expert_ffn_down_packed(const moe_problem* p, const void* h, const
   REQUIRE_PTR(w2_packed);
   REQUIRE_PTR(y_sorted);
   if (!offsets) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL");
+  const bool fp8 = d.expert == MOE_FP8_E4M3;
+  if (fp8 && (!h_scale || !w2_scale))
+    return fail(MOE_ERR_INVALID_ARG, "the FP8 path needs h_scale and w2_scale");
   if ((s = check_device(nullptr)) != MOE_OK) return s;
-  hipError_t e = launch_ffn_down_packed(d, h, offsets, w2_packed, y_sorted,
-                                        static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = fp8 ? launch_ffn_down_packed_fp8(d, h, h_scale, offsets, w2_packed, w2_scale,
+                                                  y_sorted, st)
+                     : launch_ffn_down_packed(d, h, offsets, w2_packed, y_sorted, st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn_down_packed launch");
 }
 

@@ -214,6 +214,12 @@ constexpr int64_t kDenseSharedMinRows = 2048;
 bool dense_shared(const Dims& d);
 hipError_t launch_dense_swiglu_bf16(const uint16_t* x, const uint16_t* w13, uint16_t* h,
                                     uint16_t* au, int M, int Kd, int half, hipStream_t st);
+// the shared expert's FP8 gate/up as its dense launch (rows T*K .. T*K+T-1 of the
+// permuted order; gather != nullptr: xs is x itself, in token order)
+hipError_t launch_dense_swiglu_fp8_shared(const Dims& d, const void* xs, const float* xs_scale,
+                                          const int32_t* gather, const void* w13,
+                                          const float* w13_scale, void* h, float* h_scale,
+                                          hipStream_t st);
 hipError_t launch_fp8_up(const Dims& d, const void* xs, const float* xs_scale,
                          const int32_t* offsets, const int32_t* gather, const void* w13,
                          const float* w13_scale, void* h, float* h_scale, hipStream_t st);
@@ -236,6 +242,16 @@ hipError_t launch_ffn_up_packed(const Dims& d, const void* xs, const int32_t* of
                                 void* au, hipStream_t st);
 hipError_t launch_ffn_down_packed(const Dims& d, const void* h, const int32_t* offsets,
                                   const void* p2, void* ys, hipStream_t st);
+// FP8 expert GEMMs over packed weight codes (gemm_packed_fp8.hip)
+hipError_t launch_pack_weights_fp8(const Dims& d, const void* w13, const void* w2, void* p13,
+                                   void* p2, hipStream_t st);
+hipError_t launch_ffn_up_packed_fp8(const Dims& d, const void* xs, const float* xs_scale,
+                                    const int32_t* offsets, const int32_t* gather,
+                                    const void* w13, const void* p13, const float* w13_scale,
+                                    void* h, float* h_scale, hipStream_t st);
+hipError_t launch_ffn_down_packed_fp8(const Dims& d, const void* h, const float* h_scale,
+                                      const int32_t* offsets, const void* p2,
+                                      const float* w2_scale, void* ys, hipStream_t st);
 
 hipError_t launch_combine(const Dims& d, const void* ys, const int32_t* inv_perm,
                           const float* gate, void* y, hipStream_t st);

@@ -449,24 +449,32 @@ int fp8_grid(int cus) {
 
 }  // namespace
 
+hipError_t launch_dense_swiglu_fp8_shared(const Dims& d, const void* xs, const float* xs_scale,
+                                          const int32_t* gather, const void* w13,
+                                          const float* w13_scale, void* h, float* h_scale,
+                                          hipStream_t st) {
+  const int64_t r0 = d.T * d.K;
+  const int nkb = d.H / 128;
+  const uint8_t* xa = static_cast<const uint8_t*>(xs) + (gather ? 0 : r0 * d.H);
+  const float* xsa = xs_scale + (gather ? 0 : r0 * nkb);
+  const int mt = (int)((d.T + QBM - 1) / QBM), nt = d.I / 128;
+  const int per = (mt * nt + kXcds - 1) / kXcds;
+  hipLaunchKernelGGL(k_gemm_dense_swiglu_fp8, dim3(per * kXcds), dim3(512), 0, st, xa, xsa,
+                     static_cast<const uint8_t*>(w13) + (int64_t)d.E * 2 * d.I * d.H,
+                     w13_scale + (int64_t)d.E * (2 * d.I / 128) * nkb,
+                     static_cast<uint8_t*>(h) + r0 * d.I, h_scale + r0 * (d.I / 128), (int)d.T,
+                     d.H, d.I, mt, nt);
+  return hipGetLastError();
+}
+
 hipError_t launch_fp8_up(const Dims& d, const void* xs, const float* xs_scale,
                          const int32_t* offsets, const int32_t* gather, const void* w13,
                          const float* w13_scale, void* h, float* h_scale, hipStream_t st) {
   int ng = d.E + d.S;
   if (dense_shared(d)) {  // the shared expert's rows T*K .. T*K+T-1, token order
     ng = d.E;
-    const int64_t r0 = d.T * d.K;
-    const int nkb = d.H / 128;
-    const uint8_t* xa = static_cast<const uint8_t*>(xs) + (gather ? 0 : r0 * d.H);
-    const float* xsa = xs_scale + (gather ? 0 : r0 * nkb);
-    const int mt = (int)((d.T + QBM - 1) / QBM), nt = d.I / 128;
-    const int per = (mt * nt + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL(k_gemm_dense_swiglu_fp8, dim3(per * kXcds), dim3(512), 0, st, xa, xsa,
-                       static_cast<const uint8_t*>(w13) + (int64_t)d.E * 2 * d.I * d.H,
-                       w13_scale + (int64_t)d.E * (2 * d.I / 128) * nkb,
-                       static_cast<uint8_t*>(h) + r0 * d.I, h_scale + r0 * (d.I / 128),
-                       (int)d.T, d.H, d.I, mt, nt);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e =
+        launch_dense_swiglu_fp8_shared(d, xs, xs_scale, gather, w13, w13_scale, h, h_scale, st);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((k_gemm_fp8<true>), dim3(fp8_grid(device_cu_count())), dim3(512), 0, st,

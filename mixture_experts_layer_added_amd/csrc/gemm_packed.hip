@@ -309,7 +309,9 @@ int pk_grid() {
 
 }  // namespace
 
-bool packed_supported(const Dims& d) { return d.expert == MOE_BF16 && d.act == MOE_BF16; }
+bool packed_supported(const Dims& d) {
+  return d.act == MOE_BF16 && (d.expert == MOE_BF16 || d.expert == MOE_FP8_E4M3);
+}
 
 size_t packed_w13_elems(const Dims& d) { return (size_t)(d.E + d.S) * 2 * d.I * d.H; }
 size_t packed_w2_elems(const Dims& d) { return (size_t)(d.E + d.S) * d.H * d.I; }

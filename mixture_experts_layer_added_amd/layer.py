@@ -64,8 +64,8 @@ class MoELayer:
     results are identical and the permuted copy of x is never written.
     train=True (bf16 / fp32): the gate/up GEMM also keeps the pre-activations (au) and
     backward(dy) computes dx, dw_router, dw13 and dw2 (weight gradients in fp32).
-    packed (bf16 experts): the expert GEMMs run over copies of w13 and w2 in the library's
-    packed layout, made once here (same results, bit for bit).  Default: on when the
+    packed (bf16 and FP8 experts): the expert GEMMs run over copies of w13 and w2 in the
+    library's packed layout, made once here (bf16: the same results bit for bit).  Default: on when the
     mean load per routed expert, T*K/E, is at most PACKED_MAX_MEAN_ROWS -- the packed
     kernels take at most 192 rows of an expert per tile (a larger expert streams its
     weights once per tile), the natural-layout kernels 256.
@@ -76,11 +76,11 @@ class MoELayer:
         self.shape = shape
         self.gather = gather
         self.train = train
-        bf16 = shape.expert == "bf16" and shape.act == "bf16"
+        can_pack = shape.act == "bf16" and shape.expert in ("bf16", "e4m3")
         if packed is None:
-            packed = bf16 and shape.T * shape.K <= PACKED_MAX_MEAN_ROWS * shape.E
+            packed = can_pack and shape.T * shape.K <= PACKED_MAX_MEAN_ROWS * shape.E
         self.packed = bool(packed)
-        assert bf16 or not self.packed, "packed weights are built for the bf16 path"
+        assert can_pack or not self.packed, "packed weights are built for the bf16 and FP8 paths"
         self._x = None
         self._xin = None
         self.p = shape.problem()
@@ -163,9 +163,13 @@ class MoELayer:
 
     def expert_ffn_up(self, stream=None):
         if self.packed:
-            xin, st = (self._x, self.sorted_token) if self.gather else (self.x_sorted, None)
-            L.moe_expert_ffn_up_packed(self.p, xin, st, self.offsets, self.w13, self.w13p,
-                                       self.h, self.au if self.train else None, stream)
+            if self.shape.expert == "e4m3":
+                xin, st = (self.x_q, self.sorted_token) if self.gather else (self.x_sorted, None)
+            else:
+                xin, st = (self._x, self.sorted_token) if self.gather else (self.x_sorted, None)
+            L.moe_expert_ffn_up_packed(self.p, xin, self.x_scale, st, self.offsets, self.w13,
+                                       self.w13p, self.w13_scale, self.h, self.h_scale,
+                                       self.au if self.train else None, stream)
         elif self.train:
             xin, st = (self._x, self.sorted_token) if self.gather else (self.x_sorted, None)
             L.moe_expert_ffn_up_save(self.p, xin, st, self.offsets, self.w13, self.h, self.au,
@@ -181,8 +185,8 @@ class MoELayer:
 
     def expert_ffn_down(self, stream=None):
         if self.packed:
-            L.moe_expert_ffn_down_packed(self.p, self.h, self.offsets, self.w2p, self.y_sorted,
-                                         stream)
+            L.moe_expert_ffn_down_packed(self.p, self.h, self.h_scale, self.offsets, self.w2p,
+                                         self.w2_scale, self.y_sorted, stream)
             return
         L.moe_expert_ffn_down(self.p, self.h, self.h_scale, self.offsets, self.w2, self.w2_scale,
                               self.y_sorted, stream)

@@ -230,35 +230,46 @@ def test_seq_load_stats_rejects_bad_sequence_counts(L, n_seq):
 
 
 def test_packed_entry_points_validate(L):
-    """The packed-weight calls are bf16-only and reject missing, aliased or misaligned
-    buffers before touching the device."""
+    """The packed-weight calls take bf16 activations with bf16 or FP8 experts and reject
+    missing, aliased or misaligned buffers before touching the device."""
     lib = L.lib()
     d, e = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
     p = prob(L, act_dtype=1, expert_dtype=1)
     p8 = prob(L, act_dtype=1, expert_dtype=2)
     p32 = prob(L, act_dtype=0, expert_dtype=0)
-    for q in (p8, p32):
-        assert lib.moe_pack_expert_weights(ctypes.byref(q), d, d, e, e, None) == \
-            L.MOE_ERR_UNSUPPORTED
-        assert lib.moe_expert_ffn_up_packed(ctypes.byref(q), d, None, d, d, e, d, None,
-                                            None) == L.MOE_ERR_UNSUPPORTED
-        assert lib.moe_expert_ffn_down_packed(ctypes.byref(q), d, d, e, d, None) == \
-            L.MOE_ERR_UNSUPPORTED
-    rc = lib.moe_pack_expert_weights(ctypes.byref(p), None, None, e, e, None)
-    assert rc == L.MOE_ERR_INVALID_ARG and "both NULL" in L.last_error()
-    rc = lib.moe_pack_expert_weights(ctypes.byref(p), d, None, None, None, None)
-    assert rc == L.MOE_ERR_INVALID_ARG and "packed output" in L.last_error()
-    rc = lib.moe_pack_expert_weights(ctypes.byref(p), d, None, d, None, None)
-    assert rc == L.MOE_ERR_INVALID_ARG and "in place" in L.last_error()
-    rc = lib.moe_expert_ffn_up_packed(ctypes.byref(p), d, None, d, d, None, d, None, None)
-    assert rc == L.MOE_ERR_INVALID_ARG and "w13_packed" in L.last_error()
-    rc = lib.moe_expert_ffn_up_packed(ctypes.byref(p), d, None, None, d, e, d, None, None)
-    assert rc == L.MOE_ERR_INVALID_ARG and "offsets" in L.last_error()
-    rc = lib.moe_expert_ffn_up_packed(ctypes.byref(p), ctypes.c_void_p(4100), None, d, d, e, d,
+    assert lib.moe_pack_expert_weights(ctypes.byref(p32), d, d, e, e, None) == \
+        L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_ffn_up_packed(ctypes.byref(p32), d, None, None, d, d, e, None, d,
+                                        None, None, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_ffn_down_packed(ctypes.byref(p32), d, None, d, e, None, d, None) == \
+        L.MOE_ERR_UNSUPPORTED
+    for q in (p, p8):
+        rc = lib.moe_pack_expert_weights(ctypes.byref(q), None, None, e, e, None)
+        assert rc == L.MOE_ERR_INVALID_ARG and "both NULL" in L.last_error()
+        rc = lib.moe_pack_expert_weights(ctypes.byref(q), d, None, None, None, None)
+        assert rc == L.MOE_ERR_INVALID_ARG and "packed output" in L.last_error()
+        rc = lib.moe_pack_expert_weights(ctypes.byref(q), d, None, d, None, None)
+        assert rc == L.MOE_ERR_INVALID_ARG and "in place" in L.last_error()
+    rc = lib.moe_expert_ffn_up_packed(ctypes.byref(p), d, None, None, d, d, None, None, d, None,
                                       None, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "w13_packed" in L.last_error()
+    rc = lib.moe_expert_ffn_up_packed(ctypes.byref(p), d, None, None, None, d, e, None, d, None,
+                                      None, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "offsets" in L.last_error()
+    rc = lib.moe_expert_ffn_up_packed(ctypes.byref(p), ctypes.c_void_p(4100), None, None, d, d,
+                                      e, None, d, None, None, None)
     assert rc == L.MOE_ERR_INVALID_ARG and "aligned" in L.last_error()
     big = prob(L, T=200000, H=7168, I=128, act_dtype=1, expert_dtype=1)
-    rc = lib.moe_expert_ffn_up_packed(ctypes.byref(big), d, d, d, d, e, d, None, None)
+    rc = lib.moe_expert_ffn_up_packed(ctypes.byref(big), d, None, d, d, d, e, None, d, None,
+                                      None, None)
     assert rc == L.MOE_ERR_INVALID_ARG and "2^31" in L.last_error()
-    rc = lib.moe_expert_ffn_down_packed(ctypes.byref(p), d, d, None, d, None)
+    rc = lib.moe_expert_ffn_down_packed(ctypes.byref(p), d, None, d, None, None, d, None)
     assert rc == L.MOE_ERR_INVALID_ARG and "w2_packed" in L.last_error()
+    # FP8: the scales are required, the pre-activations are not kept
+    rc = lib.moe_expert_ffn_up_packed(ctypes.byref(p8), d, None, None, d, d, e, d, d, d, None,
+                                      None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "x_scale" in L.last_error()
+    rc = lib.moe_expert_ffn_up_packed(ctypes.byref(p8), d, d, None, d, d, e, d, d, d, d, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "au" in L.last_error()
+    rc = lib.moe_expert_ffn_down_packed(ctypes.byref(p8), d, None, d, e, d, d, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "h_scale" in L.last_error()

@@ -113,14 +113,15 @@ def test_quantize_weights_bitexact(name):
     assert np.array_equal(np_(q2), o2) and np.array_equal(np_(s2).view(np.uint32), os2.view(np.uint32))
 
 
-FFN_CASES = ([(n, None) for n in CASES if not n.endswith("-bf16")] +
-             [(n, pk) for n in CASES if n.endswith("-bf16") for pk in (True, False)])
+FFN_CASES = ([(n, None) for n in CASES if n.endswith("-fp32") or "fp32-" in n] +
+             [(n, pk) for n in CASES if n.endswith("-bf16") or n.endswith("-fp8")
+              for pk in (True, False)])
 
 
 @pytest.mark.parametrize("name,packed", FFN_CASES)
 def test_expert_ffn_tolerance(name, packed):
-    """bf16 cases run twice: over packed weights and over the natural layout (the
-    LDS-ring kernels)."""
+    """bf16 and FP8 cases run twice: over packed weights and over the natural layout
+    (the LDS-ring kernels)."""
     log(f"[expert_ffn] {name} packed={packed}")
     w = case(name)
     inp = make_cpu_inputs(w)
@@ -133,7 +134,7 @@ def test_expert_ffn_tolerance(name, packed):
     if fp8:
         q13, s13, q2, s2 = fp8_weights(inp)
         layer = gpu_layer(w, inp, torch.from_numpy(q13).cuda(), torch.from_numpy(q2).cuda(),
-                          torch.from_numpy(s13).cuda(), torch.from_numpy(s2).cuda())
+                          torch.from_numpy(s13).cuda(), torch.from_numpy(s2).cuda(), packed=packed)
         layer.x_scale.copy_(torch.from_numpy(xsc))
     else:
         layer = gpu_layer(w, inp, packed=packed)

@@ -51,6 +51,8 @@ def kernel_source_sha(expert, train=False, packed=False):
     csrc = os.path.join(ROOT, "mixture_experts_layer_added_amd", "csrc")
     if train:
         files = ["gemm_bwd.hip", "common.h"]
+    elif expert == "e4m3" and packed:  # the shared expert's dense FP8 kernel is in gemm_fp8
+        files = ["gemm_packed_fp8.hip", "gemm_fp8.hip", "common.h"]
     elif expert == "e4m3":
         files = ["gemm_fp8.hip", "gemm_dense.hip", "common.h"]
     elif packed:
@@ -100,10 +102,10 @@ def parse():
                     help="time moe_route alone (router logits + group-limited top-K); with "
                          "--tokens it runs at batch sizes whose expert FFN buffers would not fit")
     ap.add_argument("--natural", action="store_true",
-                    help="bf16: run the expert GEMMs over the natural weight layout (the LDS-ring "
-                         "kernels); default: packed up to 160 rows per expert on average")
+                    help="bf16 / FP8: run the expert GEMMs over the natural weight layout (the "
+                         "LDS-ring kernels); default: packed up to 160 rows per expert on average")
     ap.add_argument("--packed", action="store_true",
-                    help="bf16: run the expert GEMMs over packed weights at any batch size")
+                    help="bf16 / FP8: run the expert GEMMs over packed weights at any batch size")
     ap.add_argument("--train", action="store_true",
                     help="time forward + bias update + backward (bf16 / fp32 experts)")
     ap.add_argument("--cpu-ffn-rows", type=int, default=0,
@@ -311,8 +313,10 @@ def main():
         roofline = {"kernel": f"gate/up GEMM + SwiGLU call: {gk} (routed experts, "
                               "grouped) + k_gemm_dense_swiglu_bf16 (the shared expert, when T >= "
                               "2048)" if w.expert == "bf16" else
-                    "gate/up GEMM + SwiGLU call (e4m3): k_gemm_fp8<true> (routed experts, grouped) "
-                    "+ k_gemm_dense_swiglu_fp8 (the shared expert, when T >= 2048)",
+                    f"gate/up GEMM + SwiGLU call (e4m3): "
+                    f"{'k_gemm_packed_fp8<true>' if layer.packed else 'k_gemm_fp8<true>'} "
+                    "(routed experts, grouped) + k_gemm_dense_swiglu_fp8 (the shared expert, "
+                    "when T >= 2048)",
                     "bound": "hbm", "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(up_gbs / HBM_PEAK_GBS, 4),
                     "bytes_per_launch": up_bytes, "ms_per_launch": round(avg_ms["ffn_up"], 4),

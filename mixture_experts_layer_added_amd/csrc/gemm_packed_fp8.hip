@@ -22,10 +22,11 @@
 // and one weight scale per wave and step.  Activation codes and their scales go by
 // direct-to-LDS loads into a three-slot ring two steps ahead, weights into registers
 // one or three steps ahead; one barrier per step.
-//   up: the gate half's wave and the up half's wave of a block exchange the up values
-//       through LDS per 32-row sub-tile; the gate wave forms h = silu(gate) * up, the
-//       row's 128-column amax is combined over the tile's four blocks in LDS, and the
-//       E4M3 codes are staged so that whole 128-byte rows are stored.
+//   up: per 32-row sub-tile the gate half's wave and the up half's wave of a block hand
+//       each other half of their values through LDS and each forms h = silu(gate) * up
+//       for half of the block's columns; the row's 128-column amax is combined over the
+//       tile's eight waves in LDS, and the E4M3 codes are staged so that whole 128-byte
+//       rows are stored.
 //   down: each 32-row sub-tile of a block (64 bf16 columns, one 128-byte line per row)
 //       is staged in LDS and stored as whole lines.
 #include "common.h"
@@ -201,61 +202,63 @@ __device__ __forceinline__ void pk8_tile(const uint8_t* __restrict__ A,
   // 32-row half (q = element / 4)
   const int rr = frow;
   if constexpr (kSwiglu) {
-    float* ex = reinterpret_cast<float*>(smem);                  // [4 blocks][32][32] up
-    float* amx = reinterpret_cast<float*>(smem + 16384);          // [4 blocks][32]
-    char* hst = smem + 16384 + 512;                               // [32 rows][128 bytes]
+    // the pair's two waves split the h elements: the gate wave forms those of q = 0, 1
+    // (columns 8q + 4h ..), the up wave those of q = 2, 3; each first hands the other
+    // its values of the other's columns (float4 slot 2qq + h, swizzled by row & 3)
+    float* exg = reinterpret_cast<float*>(smem);   // [4 blocks][32 rows][16] gate, q = 2, 3
+    float* exu = exg + 4 * 32 * 16;                // [4 blocks][32 rows][16] up, q = 0, 1
+    float* amx = exu + 4 * 32 * 16;                // [8 waves][32 rows]
+    char* hst = reinterpret_cast<char*>(amx + 8 * 32);  // [32 rows][128 bytes] codes
     uint8_t* h = static_cast<uint8_t*>(C);
     const int ncb = Nout / 128;
+    const int qb = half ? 2 : 0;                   // this wave's q range: qb, qb + 1
+    float* mine = (half ? exu : exg) + (pair * 32 + rr) * 16;
+    const float* theirs = (half ? exg : exu) + (pair * 32 + rr) * 16;
 #pragma unroll
     for (int m = 0; m < MS; ++m) {
-      // float4 q of row r (columns 8q + 4h .. +3) at slot (2q + h) ^ (r & 7)
-      float* exr = ex + (pair * 32 + rr) * 32;
-      if (half == 1) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int f = (2 * q + kq) ^ (rr & 7);
-          *reinterpret_cast<float4*>(exr + 4 * f) =
-              make_float4(acc[m][4 * q], acc[m][4 * q + 1], acc[m][4 * q + 2], acc[m][4 * q + 3]);
-        }
+      for (int qq = 0; qq < 2; ++qq) {
+        const int q = (half ? 0 : 2) + qq;  // the partner's columns
+        const int f = (2 * qq + kq) ^ (rr & 3);
+        *reinterpret_cast<float4*>(mine + 4 * f) =
+            make_float4(acc[m][4 * q], acc[m][4 * q + 1], acc[m][4 * q + 2], acc[m][4 * q + 3]);
       }
       __syncthreads();
-      float hv[16];
-      if (half == 0) {
-        float am = 0.0f;
+      float hv[8];
+      float am = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int f = (2 * q + kq) ^ (rr & 7);
-          const float4 u = *reinterpret_cast<const float4*>(exr + 4 * f);
-          hv[4 * q + 0] = silu(acc[m][4 * q + 0]) * u.x;
-          hv[4 * q + 1] = silu(acc[m][4 * q + 1]) * u.y;
-          hv[4 * q + 2] = silu(acc[m][4 * q + 2]) * u.z;
-          hv[4 * q + 3] = silu(acc[m][4 * q + 3]) * u.w;
+      for (int qq = 0; qq < 2; ++qq) {
+        const int q = qb + qq;
+        const int f = (2 * qq + kq) ^ (rr & 3);
+        const float4 o = *reinterpret_cast<const float4*>(theirs + 4 * f);
+        const float other[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-          for (int t = 0; t < 4; ++t) am = __builtin_fmaxf(am, __builtin_fabsf(hv[4 * q + t]));
+        for (int t = 0; t < 4; ++t) {
+          const float g = half ? other[t] : acc[m][4 * q + t];
+          const float u = half ? acc[m][4 * q + t] : other[t];
+          hv[4 * qq + t] = silu(g) * u;
+          am = __builtin_fmaxf(am, __builtin_fabsf(hv[4 * qq + t]));
         }
-        am = __builtin_fmaxf(am, __shfl_xor(am, 32));
-        if (kq == 0) amx[pair * 32 + rr] = am;
       }
+      am = __builtin_fmaxf(am, __shfl_xor(am, 32));
+      if (kq == 0) amx[wv * 32 + rr] = am;
       __syncthreads();
-      if (half == 0) {
-        const float am = __builtin_fmaxf(__builtin_fmaxf(amx[rr], amx[32 + rr]),
-                                         __builtin_fmaxf(amx[64 + rr], amx[96 + rr]));
-        const float sc = am > 0.0f ? am / 448.0f : 1.0f;
-        // codes of columns 32 pair + 8q + 4h .. +3: 4 bytes at byte 8q + 4h of chunk
-        // 2 pair + q/2 (16-byte chunks of the 128-byte row, slot chunk ^ (r & 7))
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t w = f32_to_e4m3_bits(hv[4 * q] / sc) |
-                             (f32_to_e4m3_bits(hv[4 * q + 1] / sc) << 8) |
-                             (f32_to_e4m3_bits(hv[4 * q + 2] / sc) << 16) |
-                             (f32_to_e4m3_bits(hv[4 * q + 3] / sc) << 24);
-          const int ch = 2 * pair + (q >> 1);
-          *reinterpret_cast<uint32_t*>(hst + rr * 128 + ((ch ^ (rr & 7)) << 4) + 8 * (q & 1) +
-                                       4 * kq) = w;
-        }
-        if (pair == 0 && kq == 0 && 32 * m + rr < m_rows)
-          C_scale[(grow0 + 32 * m + rr) * ncb + n_idx] = sc;
+      for (int w = 0; w < 8; ++w) am = __builtin_fmaxf(am, amx[w * 32 + rr]);
+      const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+      // codes of columns 32 pair + 8q + 4h .. +3: 4 bytes at byte 8(q&1) + 4h of chunk
+      // 2 pair + q/2 (16-byte chunks of the 128-byte row, slot chunk ^ (r & 7))
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const int q = qb + qq;
+        const uint32_t w = pack4_e4m3(hv[4 * qq] / sc, hv[4 * qq + 1] / sc, hv[4 * qq + 2] / sc,
+                                      hv[4 * qq + 3] / sc);
+        const int ch = 2 * pair + (q >> 1);
+        *reinterpret_cast<uint32_t*>(hst + rr * 128 + ((ch ^ (rr & 7)) << 4) + 8 * (q & 1) +
+                                     4 * kq) = w;
       }
+      if (wv == 0 && kq == 0 && 32 * m + rr < m_rows)
+        C_scale[(grow0 + 32 * m + rr) * ncb + n_idx] = sc;
       __syncthreads();
       if (wv < 4) {  // 32 rows x 8 chunks: waves 0..3, 8 rows each
         const int fr = 8 * wv + (lane >> 3), ch = lane & 7;

@@ -38,6 +38,17 @@ METRIC_TRAIN = ("MoE-layer training-step tokens/s (forward + bias update + backw
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}  # dense TFLOP/s
 VALU_FP32_PEAK = 78.6  # TFLOP/s: 256 CUs x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (no packed fp32)
+MFMA_FP32_PEAK = 157.3  # TFLOP/s, dense fp32 MFMA
+# the library computes the router logits on the matrix cores (k=1 fp32 MFMA chains) from
+# this many tokens, on the VALU below it (router.hip's dispatch rule)
+ROUTER_MFMA_MIN_TOKENS = 2048
+
+
+def router_roof(T):
+    """(logits kernel, bound, peak TFLOP/s) of moe_route at T tokens."""
+    if T >= ROUTER_MFMA_MIN_TOKENS:
+        return "k_router_logits_mfma", "mfma", MFMA_FP32_PEAK
+    return "k_router_logits", "alu", VALU_FP32_PEAK
 
 
 def log(msg):
@@ -251,7 +262,8 @@ def main():
 
     kernels = {
         "route": {"ms": avg_ms["route"], "TFLOP/s": tfs(route_flops, avg_ms["route"]),
-                  "valu_frac": tfs(route_flops, avg_ms["route"]) / VALU_FP32_PEAK},
+                  "kernel": router_roof(w.T)[0], "bound": router_roof(w.T)[1],
+                  "frac": tfs(route_flops, avg_ms["route"]) / router_roof(w.T)[2]},
         "permute": {"ms": avg_ms["permute"], "GB/s": gbs(perm_bytes, avg_ms["permute"]),
                     "hbm_frac": gbs(perm_bytes, avg_ms["permute"]) / HBM_PEAK_GBS},
         "ffn_up": {"ms": avg_ms["ffn_up"], "GB/s": gbs(up_bytes, avg_ms["ffn_up"]),
@@ -410,7 +422,8 @@ def load_log(args, w, layer, dev):
 
 
 def route_only(args, w, dev):
-    """moe_route alone: logits (fp32 VALU, fixed order) then the selection kernel."""
+    """moe_route alone: logits (fp32 sequential fma chains, on the matrix cores from 2048
+    tokens) then the selection kernel."""
     import torch
 
     import workloads
@@ -443,6 +456,7 @@ def route_only(args, w, dev):
     flops = 2.0 * w.T * w.E * w.H
     tfs = flops / (ms * 1e-3) / 1e12
     a = 2 if w.act == "bf16" else 4
+    rk, rbound, rpeak = router_roof(w.T)
     out = {
         "metric": "MoE router tokens/s (route only: fp32 logits + group-limited top-K)",
         "value": round(w.T * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -452,10 +466,10 @@ def route_only(args, w, dev):
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "G": w.G, "M": w.M,
                    "K": w.K, "J": w.J, "act": w.act, "step": "route only",
                    "parallelism": "single GPU"},
-        # the whole call is timed; the logits kernel dominates it (VALU-bound)
-        "roofline": {"kernel": "moe_route (k_router_logits dominates)", "bound": "alu",
-                     "achieved": round(tfs, 2), "peak": VALU_FP32_PEAK, "unit": "TFLOP/s",
-                     "frac": round(tfs / VALU_FP32_PEAK, 4), "traffic": None},
+        # the whole call is timed; the logits kernel dominates it
+        "roofline": {"kernel": f"moe_route ({rk} dominates)", "bound": rbound,
+                     "achieved": round(tfs, 2), "peak": rpeak, "unit": "TFLOP/s",
+                     "frac": round(tfs / rpeak, 4), "traffic": None},
         "cpu_baseline": None,
         # algorithmic bytes of the selection kernel (logits row + bias in, indices and
         # gates out); its duration comes from a kernel trace of this run

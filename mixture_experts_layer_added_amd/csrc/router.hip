@@ -6,8 +6,9 @@
 //
 // Numerics are fixed so the result is reproducible bit for bit:
 //   z[t,e]  = sequential fused multiply-add over h = 0..H-1, starting from +0
-//             (fp32 VALU, compiled without contraction; MFMA is not used because
-//             its internal summation order is not a sequential chain)
+//             (fp32, compiled without contraction: on the VALU, or on the matrix
+//             cores with the k=1 fp32 MFMA, which adds one product to each
+//             accumulator per instruction with a single rounding, i.e. an fma)
 //   s       = 1 / (1 + exp(-clamp(z, -80, 80)))   with exp by Cody-Waite
 //             reduction and a degree-7 Taylor polynomial (Horner, fused)
 //   key     = s + bias[e]
@@ -20,15 +21,15 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Logits: lanes are tokens, experts are wave-uniform.  A workgroup takes 64 tokens x
-// 8*kRE experts; its 8 waves share the tokens' hidden chunk (64 h at a time, in LDS as
-// fp32, one padded row per token) and each wave owns kRE experts, whose router-weight
-// rows it reads with scalar loads, so each fused multiply-add takes its weight operand
-// from a scalar register and its x operand from the lane's own row.  Every
-// accumulator sees h in increasing order.  kRE = 4 when there are enough tokens to fill
-// the GPU (fewer weight loads per multiply-add); up to 3072 tokens kRE = 1, which gives
-// four times as many waves to hide the latency of the chunk loads (T=128: 0.22 ->
-// 0.10 ms, T=2048: 0.31 -> 0.26 ms; logits unchanged bit for bit).
+// Logits on the VALU (small batches; larger ones use the matrix-core kernel below):
+// lanes are tokens, experts are wave-uniform.  A workgroup takes 64 tokens x 8*RE
+// experts; its 8 waves share the tokens' hidden chunk (64 h at a time, in LDS as fp32,
+// one padded row per token) and each wave owns RE experts, whose router-weight rows it
+// reads with scalar loads, so each fused multiply-add takes its weight operand from a
+// scalar register and its x operand from the lane's own row.  Every accumulator sees h
+// in increasing order.  It runs with RE = 1: four times as many waves as RE = 4 hide
+// the latency of the chunk loads at these batch sizes (T=128: 0.22 -> 0.10 ms, T=2048:
+// 0.31 -> 0.26 ms; logits unchanged bit for bit).
 // ---------------------------------------------------------------------------
 constexpr int RT = 64, RWV = 8, RH = 64, RROW = RH + 4;
 
@@ -136,6 +137,124 @@ __global__ __launch_bounds__(RWV * kWave) void k_router_logits(const XT* __restr
 #pragma unroll
     for (int e = 0; e < RE; ++e)
       if (eb + e < E) z[(int64_t)t * E + eb + e] = acc[e];
+}
+
+// ---------------------------------------------------------------------------
+// Logits on the matrix cores.  v_mfma_f32_16x16x1_4b_f32 adds one product a_i * b_j
+// to each of its 4 x 16 x 16 accumulators and rounds once, exactly like a fused
+// multiply-add (checked bit for bit against IEEE fma on gfx950, including products
+// whose rounding before the addition would change the sum, and subnormal ones), so a
+// chain of them over h = 0, 1, 2, ... is the sequential fma chain of the VALU kernel.
+// A workgroup of 4 waves takes 64 tokens x 64 experts and wave w the 32 x 32 block of
+// tokens 32(w&1).. and experts 32(w>>1)..; instruction block b covers tokens 16(b&1)..
+// and experts 16(b>>1).., so A lane l carries token l%32 and B lane l expert
+// 16(l/32) + l%16, and accumulator r of lane l is token 16(b&1) + 4(l/16) + r%4,
+// expert 16(b>>1) + l%16 with b = r/4.  x (as fp32) and W_r pass through LDS 128 h at
+// a time, one padded row per token or expert; the next chunk's global loads are in
+// flight while the current chunk is multiplied.
+// ---------------------------------------------------------------------------
+constexpr int MT = 64, ME = 64, MH = 128, MROW = MH + 4;
+// from this many tokens the logits run on the matrix cores (one 32 x 32 block per
+// wave; with fewer, too few waves fill the SIMDs: the route call at T=1024 took 0.20 ms
+// here against 0.14 ms on the VALU, at T=2048 0.21 against 0.26 ms)
+constexpr int kMfmaLogitsMinTokens = 2048;
+
+template <typename XT>
+__global__ __launch_bounds__(256) void k_router_logits_mfma(const XT* __restrict__ x,
+                                                            const float* __restrict__ w,
+                                                            float* __restrict__ z,
+                                                            int32_t* __restrict__ counts,
+                                                            int T, int H, int E) {
+  __shared__ __attribute__((aligned(16))) float xs[2][MT * MROW];
+  __shared__ __attribute__((aligned(16))) float ws[2][ME * MROW];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = blockIdx.x * MT, e0 = blockIdx.y * ME;
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int e = tid; e < E; e += 256) counts[e] = 0;  // zeroed before the select kernel
+
+  // loader: row tid/4 of the tile, h (tid%4)*32 .. +31 of the chunk (rows past T or E
+  // repeat the last one and are never stored)
+  const int lr = tid >> 2, lh = (tid & 3) * 32;
+  const XT* xp = x + (int64_t)min(t0 + lr, T - 1) * H + lh;
+  const float* wp = w + (int64_t)min(e0 + lr, E - 1) * H + lh;
+  constexpr int XV = sizeof(XT) * 32 / 16;  // 16-byte loads of the x segment
+  u32x4 xr[XV], wr[8];
+  auto gload = [&](int h0) {
+#pragma unroll
+    for (int i = 0; i < XV; ++i) xr[i] = *reinterpret_cast<const u32x4*>(xp + h0 + i * 16 / sizeof(XT));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wr[i] = *reinterpret_cast<const u32x4*>(wp + h0 + 4 * i);
+  };
+  auto lstore = [&](int buf) {
+    float* dx = &xs[buf][lr * MROW + lh];
+    if constexpr (sizeof(XT) == 2) {
+#pragma unroll
+      for (int i = 0; i < XV; ++i) {
+        const u32x4 u = xr[i];
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f[2 * j] = __uint_as_float(u[j] << 16);
+          f[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
+        }
+        *reinterpret_cast<float4*>(dx + 8 * i) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(dx + 8 * i + 4) = make_float4(f[4], f[5], f[6], f[7]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < XV; ++i) *reinterpret_cast<u32x4*>(dx + 4 * i) = xr[i];
+    }
+    float* dw = &ws[buf][lr * MROW + lh];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(dw + 4 * i) = wr[i];
+  };
+
+  const int ta = 32 * (wv & 1) + (lane & 31);
+  const int eb = 32 * (wv >> 1) + 16 * (lane >> 5) + (lane & 15);
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  const int nchunk = H / MH;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nchunk) gload((c + 1) * MH);
+    const f32x4* xa = reinterpret_cast<const f32x4*>(&xs[buf][ta * MROW]);
+    const f32x4* wb = reinterpret_cast<const f32x4*>(&ws[buf][eb * MROW]);
+    // operands of 4 h per read; the reads run two groups ahead and are issued between
+    // the multiplies (the chained MFMAs hold up the wave's issue until each is done)
+    f32x4 a[3], b[3];
+    a[0] = xa[0];
+    b[0] = wb[0];
+    a[1] = xa[1];
+    b[1] = wb[1];
+#pragma unroll
+    for (int hq = 0; hq < MH / 4; ++hq) {
+      const int cur = hq % 3;
+      acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a[cur][0], b[cur][0], acc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (hq + 2 < MH / 4) {
+        a[(hq + 2) % 3] = xa[hq + 2];
+        b[(hq + 2) % 3] = wb[hq + 2];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 1; k < 4; ++k)
+        acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a[cur][k], b[cur][k], acc, 0, 0, 0);
+    }
+    if (c + 1 < nchunk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int bk = r >> 2;
+    const int t = t0 + 32 * (wv & 1) + 16 * (bk & 1) + 4 * (lane >> 4) + (r & 3);
+    const int e = e0 + 32 * (wv >> 1) + 16 * (bk >> 1) + (lane & 15);
+    if (t < T && e < E) z[(int64_t)t * E + e] = acc[r];
+  }
 }
 
 // (value, index) ordering: larger value first, then the lower index.
@@ -282,32 +401,9 @@ __global__ __launch_bounds__(256) void k_router_select(const float* __restrict__
     if (s_cnt[e]) atomicAdd(&counts[e], s_cnt[e]);
 }
 
-}  // namespace
-
-hipError_t launch_route(const Dims& d, const void* x, const float* w_router, const float* bias,
-                        int32_t* idx, float* gate, int32_t* counts, float* logits,
-                        hipStream_t st) {
+hipError_t launch_select(const Dims& d, const float* logits, const float* bias, int32_t* idx,
+                         float* gate, int32_t* counts, hipStream_t st) {
   const int T = static_cast<int>(d.T);
-  const bool few = T <= 3072;
-  const int re = few ? 1 : 4;
-  dim3 g1((T + RT - 1) / RT, (d.E + re * RWV - 1) / (re * RWV));
-  if (d.act == MOE_BF16) {
-    if (few)
-      hipLaunchKernelGGL((k_router_logits<uint16_t, 1>), g1, dim3(RWV * kWave), 0, st,
-                         static_cast<const uint16_t*>(x), w_router, logits, counts, T, d.H, d.E);
-    else
-      hipLaunchKernelGGL((k_router_logits<uint16_t, 4>), g1, dim3(RWV * kWave), 0, st,
-                         static_cast<const uint16_t*>(x), w_router, logits, counts, T, d.H, d.E);
-  } else {
-    if (few)
-      hipLaunchKernelGGL((k_router_logits<float, 1>), g1, dim3(RWV * kWave), 0, st,
-                         static_cast<const float*>(x), w_router, logits, counts, T, d.H, d.E);
-    else
-      hipLaunchKernelGGL((k_router_logits<float, 4>), g1, dim3(RWV * kWave), 0, st,
-                         static_cast<const float*>(x), w_router, logits, counts, T, d.H, d.E);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   // the group lists have exactly J entries (J <= 8); at most 16 workgroups per CU, each
   // then looping over its tokens, so the per-workgroup count histograms stay few
   const int sel_wg = std::min((T + 3) / 4, 16 * device_cu_count());
@@ -323,6 +419,34 @@ hipError_t launch_route(const Dims& d, const void* x, const float* w_router, con
   }
 #undef MOE_SELECT
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route(const Dims& d, const void* x, const float* w_router, const float* bias,
+                        int32_t* idx, float* gate, int32_t* counts, float* logits,
+                        hipStream_t st) {
+  const int T = static_cast<int>(d.T);
+  if (T >= kMfmaLogitsMinTokens) {
+    const dim3 gm((T + MT - 1) / MT, (d.E + ME - 1) / ME);
+    if (d.act == MOE_BF16)
+      hipLaunchKernelGGL(k_router_logits_mfma<uint16_t>, gm, dim3(256), 0, st,
+                         static_cast<const uint16_t*>(x), w_router, logits, counts, T, d.H, d.E);
+    else
+      hipLaunchKernelGGL(k_router_logits_mfma<float>, gm, dim3(256), 0, st,
+                         static_cast<const float*>(x), w_router, logits, counts, T, d.H, d.E);
+  } else {
+    const dim3 g1((T + RT - 1) / RT, (d.E + RWV - 1) / RWV);
+    if (d.act == MOE_BF16)
+      hipLaunchKernelGGL((k_router_logits<uint16_t, 1>), g1, dim3(RWV * kWave), 0, st,
+                         static_cast<const uint16_t*>(x), w_router, logits, counts, T, d.H, d.E);
+    else
+      hipLaunchKernelGGL((k_router_logits<float, 1>), g1, dim3(RWV * kWave), 0, st,
+                         static_cast<const float*>(x), w_router, logits, counts, T, d.H, d.E);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_select(d, logits, bias, idx, gate, counts, st);
 }
 
 }  // namespace moe

@@ -14,6 +14,10 @@ import workloads
 SMALL_CASES = {
     "tiny-fp32": ("tiny-fp32", {}),
     "tiny-fp32-T1": ("tiny-fp32", dict(T=1)),
+    # from 2048 tokens the router logits run on the matrix cores: the fp32-activation
+    # form with a ragged last token block and E = 48 (not a multiple of the 64 experts
+    # of a workgroup); dense-bf16 and re4-ragged-bf16 below cover the bf16 form
+    "mfma-fp32": ("tiny-fp32", dict(T=2100, E=48)),
     "ragged-bf16": ("v3-bf16", dict(T=1000, H=384, E=16, G=4, M=2, K=4, J=2, I=256)),
     # ~150 rows per expert: the grouped GEMMs' three-stage ring with A stages of up to
     # 160 rows (rows rounded up to 16), next to experts just above it
@@ -26,8 +30,8 @@ SMALL_CASES = {
     # T >= 2048 with a shared expert: its gate/up GEMM runs as a dense launch (ragged
     # last row tile; dense-fp8 below is the FP8 counterpart)
     "dense-bf16": ("v3-bf16", dict(T=2100, H=384, E=16, G=4, M=2, K=4, J=2, I=384)),
-    # above 3072 tokens the router's logits kernel gives each wave four experts: a ragged
-    # last 64-token block and E = 48 (not a multiple of the 32 experts per workgroup)
+    # a ragged last 64-token block and E = 48 (router logits on the matrix cores, as
+    # from 2048 tokens)
     "re4-ragged-bf16": ("v3-bf16", dict(T=3137, H=256, E=48, G=4, M=2, K=4, J=2, I=128)),
     "ragged-fp8": ("v3-fp8", dict(T=700, H=384, E=16, G=4, M=2, K=4, J=2, I=256)),
     "dense-fp8": ("v3-fp8", dict(T=2100, H=384, E=16, G=4, M=2, K=4, J=2, I=256)),

@@ -149,11 +149,16 @@ __global__ __launch_bounds__(RWV * kWave) void k_router_logits(const XT* __restr
 // tokens 32(w&1).. and experts 32(w>>1)..; instruction block b covers tokens 16(b&1)..
 // and experts 16(b>>1).., so A lane l carries token l%32 and B lane l expert
 // 16(l/32) + l%16, and accumulator r of lane l is token 16(b&1) + 4(l/16) + r%4,
-// expert 16(b>>1) + l%16 with b = r/4.  x (as fp32) and W_r pass through LDS 128 h at
-// a time, one padded row per token or expert; the next chunk's global loads are in
-// flight while the current chunk is multiplied.
+// expert 16(b>>1) + l%16 with b = r/4.
+// x (as fp32) and W_r pass through three LDS buffers of 64 h, one padded row per token
+// or expert.  Chunk j is loaded from memory while chunk j-3 is multiplied, written to
+// LDS (buffer j%3) while chunk j-2 is, and published by that chunk's closing barrier,
+// so the operand reads (two 16-byte reads per 4 h, two groups of 4 h ahead) run on
+// across chunk boundaries and the waves never drain.  While a chained MFMA waits for
+// its predecessor the wave issues nothing else, so the reads and the LDS writes are
+// placed after the first MFMA of each group of four.
 // ---------------------------------------------------------------------------
-constexpr int MT = 64, ME = 64, MH = 128, MROW = MH + 4;
+constexpr int MT = 64, ME = 64, MH = 64, MROW = MH + 4, MG = MH / 4;
 // from this many tokens the logits run on the matrix cores (one 32 x 32 block per
 // wave; with fewer, too few waves fill the SIMDs: the route call at T=1024 took 0.20 ms
 // here against 0.14 ms on the VALU, at T=2048 0.21 against 0.26 ms)
@@ -165,88 +170,105 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(const XT* __restrict
                                                             float* __restrict__ z,
                                                             int32_t* __restrict__ counts,
                                                             int T, int H, int E) {
-  __shared__ __attribute__((aligned(16))) float xs[2][MT * MROW];
-  __shared__ __attribute__((aligned(16))) float ws[2][ME * MROW];
+  __shared__ __attribute__((aligned(16))) float xs[3][MT * MROW];
+  __shared__ __attribute__((aligned(16))) float ws[3][ME * MROW];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.x * MT, e0 = blockIdx.y * ME;
   if (blockIdx.x == 0 && blockIdx.y == 0)
     for (int e = tid; e < E; e += 256) counts[e] = 0;  // zeroed before the select kernel
 
-  // loader: row tid/4 of the tile, h (tid%4)*32 .. +31 of the chunk (rows past T or E
+  // loader: row tid/4 of the tile, h (tid%4)*16 .. +15 of the chunk (rows past T or E
   // repeat the last one and are never stored)
-  const int lr = tid >> 2, lh = (tid & 3) * 32;
+  const int lr = tid >> 2, lh = (tid & 3) * 16;
   const XT* xp = x + (int64_t)min(t0 + lr, T - 1) * H + lh;
   const float* wp = w + (int64_t)min(e0 + lr, E - 1) * H + lh;
-  constexpr int XV = sizeof(XT) * 32 / 16;  // 16-byte loads of the x segment
-  u32x4 xr[XV], wr[8];
-  auto gload = [&](int h0) {
+  constexpr int XV = sizeof(XT) * 16 / 16;  // 16-byte loads of the x segment
+  constexpr int NW = XV * (sizeof(XT) == 2 ? 2 : 1) + 4;  // LDS writes per chunk
+  u32x4 xr[2][XV], wr[2][4];
+  const int nchunk = H / MH;  // even: H is a multiple of 128
+  // past the last chunk: loads re-read the last one, and their LDS writes go to a
+  // buffer whose chunk every wave has finished (the reads of it are never used)
+  auto gload = [&](int j, int set) {
+    j = min(j, nchunk - 1);
 #pragma unroll
-    for (int i = 0; i < XV; ++i) xr[i] = *reinterpret_cast<const u32x4*>(xp + h0 + i * 16 / sizeof(XT));
+    for (int i = 0; i < XV; ++i)
+      xr[set][i] = *reinterpret_cast<const u32x4*>(xp + j * MH + i * 16 / sizeof(XT));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wr[i] = *reinterpret_cast<const u32x4*>(wp + h0 + 4 * i);
+    for (int i = 0; i < 4; ++i) wr[set][i] = *reinterpret_cast<const u32x4*>(wp + j * MH + 4 * i);
   };
-  auto lstore = [&](int buf) {
-    float* dx = &xs[buf][lr * MROW + lh];
-    if constexpr (sizeof(XT) == 2) {
-#pragma unroll
-      for (int i = 0; i < XV; ++i) {
-        const u32x4 u = xr[i];
-        float f[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f[2 * j] = __uint_as_float(u[j] << 16);
-          f[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
-        }
-        *reinterpret_cast<float4*>(dx + 8 * i) = make_float4(f[0], f[1], f[2], f[3]);
-        *reinterpret_cast<float4*>(dx + 8 * i + 4) = make_float4(f[4], f[5], f[6], f[7]);
+  // LDS write q (0 .. NW-1) of chunk j from register set `set`
+  auto lwrite = [&](int j, int set, int q) {
+    const int buf = j % 3;
+    if (q < NW - 4) {
+      float* dx = &xs[buf][lr * MROW + lh];
+      if constexpr (sizeof(XT) == 2) {
+        const u32x4 u = xr[set][q >> 1];
+        const int o = 2 * (q & 1);
+        f32x4 f;
+        f[0] = __uint_as_float(u[o] << 16);
+        f[1] = __uint_as_float(u[o] & 0xFFFF0000u);
+        f[2] = __uint_as_float(u[o + 1] << 16);
+        f[3] = __uint_as_float(u[o + 1] & 0xFFFF0000u);
+        *reinterpret_cast<f32x4*>(dx + 4 * q) = f;
+      } else {
+        *reinterpret_cast<u32x4*>(dx + 4 * q) = xr[set][q];
       }
     } else {
-#pragma unroll
-      for (int i = 0; i < XV; ++i) *reinterpret_cast<u32x4*>(dx + 4 * i) = xr[i];
+      const int i = q - (NW - 4);
+      *reinterpret_cast<u32x4*>(&ws[buf][lr * MROW + lh + 4 * i]) = wr[set][i];
     }
-    float* dw = &ws[buf][lr * MROW + lh];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(dw + 4 * i) = wr[i];
   };
 
   const int ta = 32 * (wv & 1) + (lane & 31);
   const int eb = 32 * (wv >> 1) + 16 * (lane >> 5) + (lane & 15);
+  // operand reads of group g (4 h) of chunk j
+  auto aread = [&](int j, int g) {
+    return *reinterpret_cast<const f32x4*>(&xs[j % 3][ta * MROW + 4 * g]);
+  };
+  auto bread = [&](int j, int g) {
+    return *reinterpret_cast<const f32x4*>(&ws[j % 3][eb * MROW + 4 * g]);
+  };
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-  const int nchunk = H / MH;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int c = 0; c < nchunk; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < nchunk) gload((c + 1) * MH);
-    const f32x4* xa = reinterpret_cast<const f32x4*>(&xs[buf][ta * MROW]);
-    const f32x4* wb = reinterpret_cast<const f32x4*>(&ws[buf][eb * MROW]);
-    // operands of 4 h per read; the reads run two groups ahead and are issued between
-    // the multiplies (the chained MFMAs hold up the wave's issue until each is done)
-    f32x4 a[3], b[3];
-    a[0] = xa[0];
-    b[0] = wb[0];
-    a[1] = xa[1];
-    b[1] = wb[1];
+
+  // chunks 0 and 1 in LDS, chunk 2 in registers, operand reads of groups 0, 1 issued
+  gload(0, 0);
+  gload(1, 1);
 #pragma unroll
-    for (int hq = 0; hq < MH / 4; ++hq) {
-      const int cur = hq % 3;
-      acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a[cur][0], b[cur][0], acc, 0, 0, 0);
+  for (int q = 0; q < NW; ++q) lwrite(0, 0, q);
+#pragma unroll
+  for (int q = 0; q < NW; ++q) lwrite(1, 1, q);
+  gload(2, 0);
+  __syncthreads();
+  f32x4 a[4], b[4];
+  a[0] = aread(0, 0);
+  b[0] = bread(0, 0);
+  a[1] = aread(0, 1);
+  b[1] = bread(0, 1);
+
+  // chunk c: loads of chunk c+3 into set (c+1)%2, writes of chunk c+2 from set c%2
+  auto chunk = [&](int c, int lset, int wset) {
+    gload(c + 3, lset);
+#pragma unroll
+    for (int g = 0; g < MG; ++g) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a[g % 4][0], b[g % 4][0], acc, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if (hq + 2 < MH / 4) {
-        a[(hq + 2) % 3] = xa[hq + 2];
-        b[(hq + 2) % 3] = wb[hq + 2];
-      }
+      const int gn = g + 2;
+      a[gn % 4] = gn < MG ? aread(c, gn) : aread(c + 1, gn - MG);
+      b[gn % 4] = gn < MG ? bread(c, gn) : bread(c + 1, gn - MG);
+      if (g < NW) lwrite(c + 2, wset, g);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 1; k < 4; ++k)
-        acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a[cur][k], b[cur][k], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a[g % 4][k], b[g % 4][k], acc, 0, 0, 0);
     }
-    if (c + 1 < nchunk) lstore(buf ^ 1);
     __syncthreads();
+  };
+  for (int c = 0; c < nchunk; c += 2) {
+    chunk(c, 1, 0);
+    chunk(c + 1, 0, 1);
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {

@@ -25,6 +25,8 @@
 // activation rows, which all four waves need, go by direct-to-LDS loads into a three-
 // slot ring, two steps ahead, issued after the step's multiplies.  One barrier per step.
 // Activation rows past the group's end read as zeros (out-of-range buffer offsets).
+#include <type_traits>
+
 #include "common.h"
 #include "schedule.h"
 
@@ -127,9 +129,10 @@ __device__ __forceinline__ void pk_tile(const uint16_t* __restrict__ A,
                                             ((c ^ (frow >> 1)) & 7) * 16);
   };
 
-  // the loads below are issued in a fixed pattern (past the last step they re-read
-  // it), so the count of loads behind a given activation step is the same at every
-  // step: after A(kt) a wave issues B(kt-1+D) (8 loads) and A(kt+1) (MS loads)
+  // the loads below are issued in a fixed pattern: after A(kk) a wave issues B(kk-1+D)
+  // (8 loads) and A(kk+1) (MS loads), so all but the last MS + 8 loads are complete when
+  // A(kk) is.  The last D + 1 steps are peeled: they issue no loads past the tile's end,
+  // and their counts shrink accordingly (compile-time, as j is)
   __syncthreads();  // the previous tile's LDS reads are done before the ring is refilled
   aload(0, 0);
   bload(0, 0);
@@ -137,44 +140,59 @@ __device__ __forceinline__ void pk_tile(const uint16_t* __restrict__ A,
 #pragma unroll
   for (int j = 1; j < D; ++j) bload(min(j, nk - 1), j);
 
-  for (int kt = 0; kt < nk; kt += D + 1) {
+  auto step = [&](int kk, auto jc, auto lc) {
+    constexpr int j = decltype(jc)::value;
+    constexpr bool last = decltype(lc)::value;
+    if constexpr (!last) wait_vm<MS + 8>();
+    else wait_vm<(j < 2 ? 8 : 0) + (j < D ? MS : 0)>();
+    __syncthreads();
+    if constexpr (!last || j == 0) bload(kk + D, (j + D) % (D + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    const int cs = kk % 3;
+    if (w_on) {
+      const char* as = smem + cs * SL;
+      // fragments of the next half-step are read while this one multiplies
+      bf16x8 af[2][MS];
 #pragma unroll
-    for (int j = 0; j <= D; ++j) {
-      const int kk = kt + j;
-      wait_vm<MS + 8>();
-      __syncthreads();
-      bload(min(kk + D, nk - 1), (j + D) % (D + 1));
-      __builtin_amdgcn_sched_barrier(0);
-      const int cs = kk % 3;
-      if (w_on) {
-        const char* as = smem + cs * SL;
-        // fragments of the next half-step are read while this one multiplies
-        bf16x8 af[2][MS];
+      for (int m = 0; m < MS; ++m) af[0][m] = afrag(as, m, 0);
 #pragma unroll
-        for (int m = 0; m < MS; ++m) af[0][m] = afrag(as, m, 0);
+      for (int s = 0; s < 4; ++s) {
+        if (s < 3) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if (s < 3) {
-#pragma unroll
-            for (int m = 0; m < MS; ++m) af[(s + 1) & 1][m] = afrag(as, m, s + 1);
-          }
-          const bf16x8 b0 = __builtin_bit_cast(bf16x8, br[j][s]);
-          const bf16x8 b1 = __builtin_bit_cast(bf16x8, br[j][4 + s]);
-#pragma unroll
-          for (int m = 0; m < MS; ++m) {
-            if (kSwiglu) {
-              acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][m], b0, acc[m][0], 0, 0, 0);
-              acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][m], b1, acc[m][1], 0, 0, 0);
-            } else {
-              acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, af[s & 1][m], acc[m][0], 0, 0, 0);
-              acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, af[s & 1][m], acc[m][1], 0, 0, 0);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
+          for (int m = 0; m < MS; ++m) af[(s + 1) & 1][m] = afrag(as, m, s + 1);
         }
+        const bf16x8 b0 = __builtin_bit_cast(bf16x8, br[j][s]);
+        const bf16x8 b1 = __builtin_bit_cast(bf16x8, br[j][4 + s]);
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+          if (kSwiglu) {
+            acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][m], b0, acc[m][0], 0, 0, 0);
+            acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][m], b1, acc[m][1], 0, 0, 0);
+          } else {
+            acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, af[s & 1][m], acc[m][0], 0, 0, 0);
+            acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, af[s & 1][m], acc[m][1], 0, 0, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      aload(min(kk + 2, nk - 1), (kk + 2) % 3);
     }
+    if constexpr (!last || j < D - 1) aload(kk + 2, (kk + 2) % 3);
+  };
+  using std::integral_constant;
+  const int kl = nk - (D + 1);  // first of the peeled steps
+  for (int kt = 0; kt < kl; kt += D + 1) {
+    step(kt, integral_constant<int, 0>(), std::false_type());
+    step(kt + 1, integral_constant<int, 1>(), std::false_type());
+    if constexpr (D == 3) {
+      step(kt + 2, integral_constant<int, 2>(), std::false_type());
+      step(kt + 3, integral_constant<int, 3>(), std::false_type());
+    }
+  }
+  step(kl, integral_constant<int, 0>(), std::true_type());
+  step(kl + 1, integral_constant<int, 1>(), std::true_type());
+  if constexpr (D == 3) {
+    step(kl + 2, integral_constant<int, 2>(), std::true_type());
+    step(kl + 3, integral_constant<int, 3>(), std::true_type());
   }
   wait_vm<0>();  // no load of this tile lands in the ring after the next tile's barrier
 

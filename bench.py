@@ -36,7 +36,10 @@ METRIC = "MoE-layer tokens/s (7168d, 256e top-8, T=4096); MFMA % and HBM % of pe
 METRIC_TRAIN = ("MoE-layer training-step tokens/s (forward + bias update + backward; 7168d, "
                 "256e top-8, T=4096)")
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}  # dense TFLOP/s
+# peak of the expert GEMMs' arithmetic, TFLOP/s: dense MFMA for bf16 and fp8; the fp32
+# expert GEMM is a SIMT kernel, so its roof is the (non-packed) VALU rate
+MFMA_PEAK = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 78.6}
+GEMM_BOUND = {"bf16": "mfma", "e4m3": "mfma", "f32": "alu"}
 VALU_FP32_PEAK = 78.6  # TFLOP/s: 256 CUs x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (no packed fp32)
 MFMA_FP32_PEAK = 157.3  # TFLOP/s, dense fp32 MFMA
 # the library computes the router logits on the matrix cores (k=1 fp32 MFMA chains) from
@@ -260,6 +263,7 @@ def main():
     def tfs(f, ms):
         return f / (ms * 1e-3) / 1e12
 
+    frac_key = "mfma_frac" if GEMM_BOUND[w.expert] == "mfma" else "valu_frac"
     kernels = {
         "route": {"ms": avg_ms["route"], "TFLOP/s": tfs(route_flops, avg_ms["route"]),
                   "kernel": router_roof(w.T)[0], "bound": router_roof(w.T)[1],
@@ -269,11 +273,11 @@ def main():
         "ffn_up": {"ms": avg_ms["ffn_up"], "GB/s": gbs(up_bytes, avg_ms["ffn_up"]),
                    "hbm_frac": gbs(up_bytes, avg_ms["ffn_up"]) / HBM_PEAK_GBS,
                    "TFLOP/s": tfs(up_flops, avg_ms["ffn_up"]),
-                   "mfma_frac": tfs(up_flops, avg_ms["ffn_up"]) / MFMA_PEAK[w.expert]},
+                   frac_key: tfs(up_flops, avg_ms["ffn_up"]) / MFMA_PEAK[w.expert]},
         "ffn_down": {"ms": avg_ms["ffn_down"], "GB/s": gbs(down_bytes, avg_ms["ffn_down"]),
                      "hbm_frac": gbs(down_bytes, avg_ms["ffn_down"]) / HBM_PEAK_GBS,
                      "TFLOP/s": tfs(down_flops, avg_ms["ffn_down"]),
-                     "mfma_frac": tfs(down_flops, avg_ms["ffn_down"]) / MFMA_PEAK[w.expert]},
+                     frac_key: tfs(down_flops, avg_ms["ffn_down"]) / MFMA_PEAK[w.expert]},
         "combine": {"ms": avg_ms["combine"], "GB/s": gbs(comb_bytes, avg_ms["combine"]),
                     "hbm_frac": gbs(comb_bytes, avg_ms["combine"]) / HBM_PEAK_GBS},
         "bias_update": {"ms": avg_ms["bias_update"]},
@@ -300,7 +304,7 @@ def main():
                  "hbm_frac": gbs(b, avg_ms[n]) / HBM_PEAK_GBS}
             if f:
                 k["TFLOP/s"] = tfs(f, avg_ms[n])
-                k["mfma_frac"] = tfs(f, avg_ms[n]) / MFMA_PEAK[w.expert]
+                k[frac_key] = tfs(f, avg_ms[n]) / MFMA_PEAK[w.expert]
             kernels[n] = k
     if args.train:
         # the weight-gradient call: two launches of k_gemm_tn_bf16 (dW2, then dW13);
@@ -322,20 +326,24 @@ def main():
         intensity = up_flops / up_bytes
         ridge = MFMA_PEAK[w.expert] * 1e12 / (HBM_PEAK_GBS * 1e9)
         gk = "k_gemm_packed<true>" if layer.packed else "k_gemm_bf16<true>"
-        roofline = {"kernel": f"gate/up GEMM + SwiGLU call: {gk} (routed experts, "
-                              "grouped) + k_gemm_dense_swiglu_bf16 (the shared expert, when T >= "
-                              "2048)" if w.expert == "bf16" else
-                    f"gate/up GEMM + SwiGLU call (e4m3): "
-                    f"{'k_gemm_packed_fp8<true>' if layer.packed else 'k_gemm_fp8<true>'} "
-                    "(routed experts, grouped) + k_gemm_dense_swiglu_fp8 (the shared expert, "
-                    "when T >= 2048)",
+        if w.expert == "bf16":
+            up_name = (f"gate/up GEMM + SwiGLU call: {gk} (routed experts, grouped) + "
+                       "k_gemm_dense_swiglu_bf16 (the shared expert, when T >= 2048)")
+        elif w.expert == "e4m3":
+            up_name = ("gate/up GEMM + SwiGLU call (e4m3): "
+                       f"{'k_gemm_packed_fp8<true>' if layer.packed else 'k_gemm_fp8<true>'} "
+                       "(routed experts, grouped) + k_gemm_dense_swiglu_fp8 (the shared "
+                       "expert, when T >= 2048)")
+        else:
+            up_name = "gate/up GEMM + SwiGLU call (fp32): k_gemm_f32<true> (every group)"
+        roofline = {"kernel": up_name,
                     "bound": "hbm", "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(up_gbs / HBM_PEAK_GBS, 4),
                     "bytes_per_launch": up_bytes, "ms_per_launch": round(avg_ms["ffn_up"], 4),
                     "traffic": None, "intensity_flop_per_byte": round(intensity, 1),
                     "ridge_flop_per_byte": round(ridge, 1)}
         if intensity >= ridge:
-            roofline.update({"bound": "mfma", "achieved": round(up_tfs, 1),
+            roofline.update({"bound": GEMM_BOUND[w.expert], "achieved": round(up_tfs, 1),
                              "peak": MFMA_PEAK[w.expert], "unit": "TFLOP/s",
                              "frac": round(up_tfs / MFMA_PEAK[w.expert], 4),
                              "flops_per_launch": up_flops})

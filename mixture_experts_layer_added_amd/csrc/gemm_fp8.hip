@@ -442,6 +442,174 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dense_swiglu_fp8(
   }
 }
 
+// The same dense FP8 gate/up over 256-row tiles, for batches that give every CU a
+// tile: 256 rows x 256 weight rows per tile, wave (wm, wn) owning rows 64wm .. +63 (two
+// 32-row sub-tiles) and the sub-tiles 4wn .. 4wn+3 of the gate/up interleave.  Each
+// wave multiplies 16 MFMAs per 128-deep step for 24 KiB of LDS fragment reads (the
+// 128-row kernel: 8 MFMAs for 20 KiB; its LDS reads, not its MFMAs, bound it).  The
+// weight fragment is the MFMA's first operand, as in the packed kernels, so a lane's
+// accumulators belong to one activation row and the per-block promotion takes a single
+// scale per lane: acc += partial * (s_a * s_w), the same products in the same order,
+// so the codes equal the 128-row kernel's bit for bit.  Two 64 KiB stages in LDS: step
+// kt's loads go out right after the barrier that frees their buffer, one step ahead.
+// h codes are staged per row in LDS (16-byte chunks swizzled by the row) and written
+// back as whole 128-byte lines.
+constexpr int WBM = 256;
+constexpr int kWA = WBM * FBK;          // A stage: 32 KiB
+constexpr int kWStage = kWA + kFB;      // 64 KiB
+
+__global__ __launch_bounds__(512, 1) void k_gemm_dense_swiglu_fp8_w(
+    const uint8_t* __restrict__ A, const float* __restrict__ A_scale,
+    const uint8_t* __restrict__ B, const float* __restrict__ B_scale, uint8_t* __restrict__ h,
+    float* __restrict__ h_scale, int M, int Kd, int half, int mt, int nt) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kWStage];
+  __shared__ __attribute__((aligned(16))) float s_sa[2][WBM];
+  __shared__ float s_amax[2][WBM];
+  const int total = mt * nt;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (tile >= total) return;
+  constexpr int band_h = 4;  // row tiles per band; column-major inside a band
+  const int band = tile / (band_h * nt), within = tile % (band_h * nt);
+  const int rb = min(band_h, mt - band * band_h);
+  const int n_idx = within / rb, m_idx = band * band_h + within % rb;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv >> 1, wn = wv & 1;
+  const int nk = Kd / FBK;
+  const int m0 = m_idx * WBM;
+  const int m_rows = min(WBM, M - m0);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
+  const uint32_t lds_sa = __builtin_amdgcn_readfirstlane(lds_offset(&s_sa[0][0]));
+  // loader: instruction i of wave wv fills rows 64i + 8wv .. +7 of an operand stage;
+  // lane l writes row 64i + 8wv + (l>>3), slot l&7 (chunk (l&7) ^ ((row>>1)&7))
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ ((4 * (wv & 1) + (lane >> 4)) & 7);
+  const int kq = lane >> 5, fr = lane & 31;
+  const i32x4 arsrc = buffer_rsrc(A + (int64_t)m0 * Kd, (uint32_t)m_rows * Kd);
+  const i32x4 brsrc = buffer_rsrc(B, (uint32_t)(2 * half) * Kd);
+  const i32x4 srsrc = buffer_rsrc(A_scale + (int64_t)m0 * nk, (uint32_t)m_rows * nk * 4);
+  uint32_t aoff[4], boff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 64 * i + 8 * wv + lrow;
+    aoff[i] = (uint32_t)(r * Kd + lchunk * 16);
+    const int br = r < 128 ? n_idx * 128 + r : half + n_idx * 128 + (r - 128);
+    boff[i] = (uint32_t)(br * Kd + lchunk * 16);
+  }
+  const bool ld_sa = wv < 4;  // waves 0..3 bring 64 activation scales each
+  const uint32_t soff = (uint32_t)((64 * wv + lane) * nk) * 4;
+  const uint32_t ldsw = lds0 + 8 * wv * FBK;
+  const uint32_t ldss = lds_sa + 64 * wv * 4;
+  const float* bsc0 = B_scale + (int64_t)n_idx * nk;                  // gate block row
+  const float* bsc1 = B_scale + (int64_t)(half / 128 + n_idx) * nk;   // up block row
+  auto stage_load = [&](int kt, int st) {
+    const uint32_t sa_ = ldsw + st * kWStage;
+    const uint32_t ko = (uint32_t)kt * FBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load16_to_lds(arsrc, sa_ + i * 64 * FBK, aoff[i] + ko);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load16_to_lds(brsrc, sa_ + kWA + i * 64 * FBK, boff[i] + ko);
+    if (ld_sa) load4_to_lds(srsrc, ldss + st * (WBM * 4), soff + (uint32_t)kt * 4);
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.0f;
+
+  stage_load(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    const float sw0 = bsc0[kt];
+    const float sw1 = bsc1[kt];
+    wait_vm<0>();     // step kt's stage is in
+    __syncthreads();  // ... for every wave, and step kt-1's buffer is free
+    if (kt + 1 < nk) stage_load(kt + 1, st ^ 1);
+    const char* as = smem + st * kWStage;
+    const char* bs = as + kWA;
+    i32x8 a0[2], a1[2];
+    float sa[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int arow = 64 * wm + 32 * m + fr;
+      a0[m] = frag32(as + fswz(arow, 2 * kq), as + fswz(arow, 2 * kq + 1));
+      a1[m] = frag32(as + fswz(arow, 4 + 2 * kq), as + fswz(arow, 5 + 2 * kq));
+      sa[m] = s_sa[st][arow];
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int nn = 4 * wn + n;
+      const int brow = (nn & 1) * 128 + 32 * (nn >> 1) + fr;
+      const i32x8 b0 = frag32(bs + fswz(brow, 2 * kq), bs + fswz(brow, 2 * kq + 1));
+      const i32x8 b1 = frag32(bs + fswz(brow, 4 + 2 * kq), bs + fswz(brow, 5 + 2 * kq));
+      const float sw = (n & 1) ? sw1 : sw0;  // sub-tile parity: gate even, up odd
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        f32x16 t;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) t[i] = 0.0f;
+        t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0, a0[m], t, 0, 0, 0, 127, 0, 127);
+        t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1, a1[m], t, 0, 0, 0, 127, 0, 127);
+        const float sc = sa[m] * sw;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[m][n][i] = __builtin_fmaf(t[i], sc, acc[m][n][i]);
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with the stages, which now stage the codes
+
+  // lane: activation row 64wm + 32m + l%32; h columns (of the tile's 128)
+  // 64wn + 32p + 8q + 4(l/32) + t for accumulator element 4q + t of pair p
+  float hv[2][2][16];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    float am = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        hv[m][p][i] = silu(acc[m][2 * p][i]) * acc[m][2 * p + 1][i];
+        am = __builtin_fmaxf(am, __builtin_fabsf(hv[m][p][i]));
+      }
+    am = __builtin_fmaxf(am, __shfl_xor(am, 32));
+    if (kq == 0) s_amax[wn][64 * wm + 32 * m + fr] = am;
+  }
+  __syncthreads();
+  char* hst = smem;  // [256 rows][128 bytes] of codes, chunk slot c ^ (row & 7)
+  const int ncb = half / 128;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int r = 64 * wm + 32 * m + fr;
+    const float am = __builtin_fmaxf(s_amax[0][r], s_amax[1][r]);
+    const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w = pack4_e4m3(hv[m][p][4 * q] / sc, hv[m][p][4 * q + 1] / sc,
+                                      hv[m][p][4 * q + 2] / sc, hv[m][p][4 * q + 3] / sc);
+        const int ch = 4 * wn + 2 * p + (q >> 1);
+        *reinterpret_cast<uint32_t*>(hst + r * 128 + ((ch ^ (r & 7)) << 4) + 8 * (q & 1) +
+                                     4 * kq) = w;
+      }
+    if (wn == 0 && kq == 0 && r < m_rows) h_scale[(int64_t)(m0 + r) * ncb + n_idx] = sc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // 256 rows x 8 chunks, 4 per thread
+    const int row = 64 * i + (tid >> 3), ch = tid & 7;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(hst + row * 128 + ((ch ^ (row & 7)) << 4));
+    if (row < m_rows)
+      __builtin_nontemporal_store(
+          v, reinterpret_cast<u32x4*>(h + (int64_t)(m0 + row) * half + n_idx * 128 + 16 * ch));
+  }
+}
+
 int fp8_grid(int cus) {
   const int p = (cus / kXcds) * kXcds;
   return p < kXcds ? kXcds : p;
@@ -457,7 +625,18 @@ hipError_t launch_dense_swiglu_fp8_shared(const Dims& d, const void* xs, const f
   const int nkb = d.H / 128;
   const uint8_t* xa = static_cast<const uint8_t*>(xs) + (gather ? 0 : r0 * d.H);
   const float* xsa = xs_scale + (gather ? 0 : r0 * nkb);
-  const int mt = (int)((d.T + QBM - 1) / QBM), nt = d.I / 128;
+  const int nt = d.I / 128;
+  const int mtw = (int)((d.T + WBM - 1) / WBM);
+  if (mtw * nt >= device_cu_count()) {  // every CU gets a 256-row tile
+    const int perw = (mtw * nt + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL(k_gemm_dense_swiglu_fp8_w, dim3(perw * kXcds), dim3(512), 0, st, xa, xsa,
+                       static_cast<const uint8_t*>(w13) + (int64_t)d.E * 2 * d.I * d.H,
+                       w13_scale + (int64_t)d.E * (2 * d.I / 128) * nkb,
+                       static_cast<uint8_t*>(h) + r0 * d.I, h_scale + r0 * (d.I / 128),
+                       (int)d.T, d.H, d.I, mtw, nt);
+    return hipGetLastError();
+  }
+  const int mt = (int)((d.T + QBM - 1) / QBM);
   const int per = (mt * nt + kXcds - 1) / kXcds;
   hipLaunchKernelGGL(k_gemm_dense_swiglu_fp8, dim3(per * kXcds), dim3(512), 0, st, xa, xsa,
                      static_cast<const uint8_t*>(w13) + (int64_t)d.E * 2 * d.I * d.H,

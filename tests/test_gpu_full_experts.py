@@ -177,3 +177,43 @@ def test_whole_experts_backward_input():
         assert e1 <= TOL[w.expert] and e2 <= TOL[w.expert], tag
     del layer
     torch.cuda.empty_cache()
+
+
+def test_shared_expert_fp8_tile_forms_agree():
+    """The shared expert's FP8 gate/up has two dense forms: 256-row tiles when every CU
+    gets one (T=4096 at the V3 shape), 128-row tiles below.  A shared row depends only
+    on its own token (its per-token activation scales included), so the h codes and
+    scales of tokens 0..2047 at T=4096 must equal those at T=2048 with the same first
+    2048 tokens, bit for bit: the two forms promote the same per-block partial sums with
+    the same scale products in the same order."""
+    w4 = workloads.get("v3-fp8")
+    w2k = workloads.get("v3-fp8", T=2048)
+    tiles_wide = ((w4.T + 255) // 256) * (w4.I // 128)
+    tiles_small = ((w2k.T + 255) // 256) * (w2k.I // 128)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    log(f"[shared fp8 forms] 256-row tiles at T={w4.T}: {tiles_wide}, at T={w2k.T}: "
+        f"{tiles_small} (the wide form needs >= {cus})")
+    if not tiles_small < cus <= tiles_wide:
+        pytest.skip(f"{cus} CUs: the two batch sizes do not select the two tile forms")
+    from mixture_experts_layer_added_amd.layer import MoELayer, quantize_weights_fp8
+    dev = torch.device("cuda")
+    wr, b = workloads.make_router(w4, dev)
+    w13, w2 = workloads.make_experts(w4, dev)
+    q13, s13 = quantize_weights_fp8(w13)
+    q2, s2 = quantize_weights_fp8(w2)
+    del w13, w2
+    x = workloads.make_x(w4, device=dev)
+    hs = []
+    for w, xx in ((w4, x), (w2k, x[:w2k.T].contiguous())):
+        layer = MoELayer(shape_of(w), wr, b, q13, q2, s13, s2, gather=True)
+        layer.route(xx)
+        layer.permute(xx)
+        layer.expert_ffn_up()
+        torch.cuda.synchronize()
+        r0 = w.T * w.K
+        hs.append((np_(layer.h[r0:r0 + w2k.T]), np_(layer.h_scale[r0:r0 + w2k.T])))
+        del layer
+        torch.cuda.empty_cache()
+    assert np.array_equal(hs[0][0], hs[1][0])
+    assert np.array_equal(hs[0][1].view(np.uint32), hs[1][1].view(np.uint32))
+    log(f"    h codes [{w2k.T} x {w4.I}] and scales of the shared expert: bit-identical")

@@ -343,6 +343,28 @@ moe_status moe_expert_ffn_backward_input(const moe_problem* p, const int32_t* of
                                          const void* dy_sorted, void* dau, void* dx_sorted,
                                          void* stream);
 
+/* Weights for the backward input part over packed weights (bf16 only): the transposes
+ * W2[g]^T [I,H] and W13[g]^T [H,2I], each in the down-GEMM packed layout of
+ * moe_pack_expert_weights (rows in blocks of 64, k steps of 64), so the two backward
+ * GEMMs stream their weights like the forward ones.
+ *   w13 [E+S,2I,H] bf16 -> w13t_packed (same size);  w2 [E+S,H,I] bf16 -> w2t_packed
+ *   (same size).  Either pair may be NULL.  Outputs are owned by the caller; packing is
+ *   not in place.  Errors: MOE_ERR_UNSUPPORTED unless act and expert dtypes are BF16. */
+moe_status moe_pack_expert_weights_transposed(const moe_problem* p, const void* w13,
+                                              const void* w2, void* w13t_packed,
+                                              void* w2t_packed, void* stream);
+
+/* Expert FFN backward, input part, over the packed transposed weights: the same results
+ * as moe_expert_ffn_backward_input bit for bit (the same 16-deep products, in the same
+ * order, with the same epilogue arithmetic), bf16 only.
+ *   w13t_packed, w2t_packed from moe_pack_expert_weights_transposed; the other arguments
+ *   as moe_expert_ffn_backward_input. */
+moe_status moe_expert_ffn_backward_input_packed(const moe_problem* p, const int32_t* offsets,
+                                                const void* w13t_packed,
+                                                const void* w2t_packed, const void* au,
+                                                const void* dy_sorted, void* dau,
+                                                void* dx_sorted, void* stream);
+
 /* Expert FFN backward, weight part, per group g over its rows (fp32 accumulation):
  *   dw2[g]  = dY^T h    [E+S,H,I]  fp32 out,
  *   dw13[g] = dau^T x   [E+S,2I,H] fp32 out   (groups without rows get zeros).

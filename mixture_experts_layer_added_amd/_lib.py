@@ -24,7 +24,8 @@ EXPORTS = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_up",
            "moe_router_backward", "moe_expert_ffn_backward_input",
            "moe_expert_ffn_backward_weight", "moe_unpermute_sum", "moe_permute_noalloc",
            "moe_seq_load_stats", "moe_pack_expert_weights", "moe_expert_ffn_up_packed",
-           "moe_expert_ffn_down_packed")
+           "moe_expert_ffn_down_packed", "moe_pack_expert_weights_transposed",
+           "moe_expert_ffn_backward_input_packed")
 
 
 class MoeError(RuntimeError):
@@ -74,6 +75,8 @@ def lib():
         L.moe_unpermute_sum.argtypes = [pp, vp, vp, vp, vp, vp]
         L.moe_expert_ffn_down.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_pack_expert_weights.argtypes = [pp, vp, vp, vp, vp, vp]
+        L.moe_pack_expert_weights_transposed.argtypes = [pp, vp, vp, vp, vp, vp]
+        L.moe_expert_ffn_backward_input_packed.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_expert_ffn_up_packed.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_expert_ffn_down_packed.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_combine.argtypes = [pp, vp, vp, vp, vp, vp]
@@ -92,7 +95,8 @@ def lib():
                   "moe_expert_ffn_backward_input", "moe_expert_ffn_backward_weight",
                   "moe_unpermute_sum", "moe_permute_noalloc", "moe_seq_load_stats",
                   "moe_pack_expert_weights", "moe_expert_ffn_up_packed",
-                  "moe_expert_ffn_down_packed"):
+                  "moe_expert_ffn_down_packed", "moe_pack_expert_weights_transposed",
+                  "moe_expert_ffn_backward_input_packed"):
             getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -254,6 +258,21 @@ def moe_router_backward(p, x, w_router, logits, topk_idx, topk_gate, dgate, offs
                                      _ptr(offsets), _ptr(sorted_token), _ptr(dz),
                                      _ptr(dx_router), _ptr(dw_router), _stream(stream)),
            "moe_router_backward")
+
+
+def moe_pack_expert_weights_transposed(p, w13, w2, w13t_packed, w2t_packed, stream=None):
+    _check(lib().moe_pack_expert_weights_transposed(ctypes.byref(p), _ptr(w13), _ptr(w2),
+                                                    _ptr(w13t_packed), _ptr(w2t_packed),
+                                                    _stream(stream)),
+           "moe_pack_expert_weights_transposed")
+
+
+def moe_expert_ffn_backward_input_packed(p, offsets, w13t_packed, w2t_packed, au, dy_sorted,
+                                         dau, dx_sorted, stream=None):
+    _check(lib().moe_expert_ffn_backward_input_packed(
+        ctypes.byref(p), _ptr(offsets), _ptr(w13t_packed), _ptr(w2t_packed), _ptr(au),
+        _ptr(dy_sorted), _ptr(dau), _ptr(dx_sorted), _stream(stream)),
+        "moe_expert_ffn_backward_input_packed")
 
 
 def moe_expert_ffn_backward_input(p, offsets, w13, w2, au, dy_sorted, dau, dx_sorted,

@@ -531,6 +531,54 @@ moe_status moe_pack_expert_weights(const moe_problem* p, const void* w13, const 
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_pack_expert_weights launch");
 }
 
+static moe_status require_bf16_pair(const Dims& d, const char* call) {
+  if (d.act != MOE_BF16 || d.expert != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: built for act and expert dtype BF16", call);
+  return MOE_OK;
+}
+
+moe_status moe_pack_expert_weights_transposed(const moe_problem* p, const void* w13,
+                                              const void* w2, void* w13t_packed,
+                                              void* w2t_packed, void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  if ((s = require_bf16_pair(d, "moe_pack_expert_weights_transposed")) != MOE_OK) return s;
+  if (!w13 && !w2) return fail(MOE_ERR_INVALID_ARG, "w13 and w2 are both NULL");
+  if ((w13 && !w13t_packed) || (w2 && !w2t_packed))
+    return fail(MOE_ERR_INVALID_ARG, "a packed output is NULL for a given input");
+  if ((w13 && w13 == w13t_packed) || (w2 && w2 == w2t_packed))
+    return fail(MOE_ERR_INVALID_ARG, "packing cannot run in place");
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  const hipError_t e =
+      launch_pack_weights_t(d, w13, w2, w13t_packed, w2t_packed, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_pack_expert_weights_transposed launch");
+}
+
+moe_status moe_expert_ffn_backward_input_packed(const moe_problem* p, const int32_t* offsets,
+                                                const void* w13t_packed,
+                                                const void* w2t_packed, const void* au,
+                                                const void* dy_sorted, void* dau,
+                                                void* dx_sorted, void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  if ((s = require_bf16_pair(d, "moe_expert_ffn_backward_input_packed")) != MOE_OK) return s;
+  REQUIRE_PTR(w13t_packed);
+  REQUIRE_PTR(w2t_packed);
+  REQUIRE_PTR(au);
+  REQUIRE_PTR(dy_sorted);
+  REQUIRE_PTR(dau);
+  REQUIRE_PTR(dx_sorted);
+  if (!offsets) return fail(MOE_ERR_INVALID_ARG, "offsets is NULL");
+  if ((s = check_bwd_rows(d)) != MOE_OK) return s;
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  const hipError_t e = launch_ffn_bwd_input_packed(d, offsets, w13t_packed, w2t_packed, au,
+                                                   dy_sorted, dau, dx_sorted,
+                                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_ffn_backward_input_packed launch");
+}
+
 moe_status moe_expert_ffn_up_packed(const moe_problem* p, const void* x, const float* x_scale,
                                     const int32_t* sorted_token, const int32_t* offsets,
                                     const void* w13, const void* w13_packed,

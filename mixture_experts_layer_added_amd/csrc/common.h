@@ -242,6 +242,13 @@ hipError_t launch_ffn_up_packed(const Dims& d, const void* xs, const int32_t* of
                                 void* au, hipStream_t st);
 hipError_t launch_ffn_down_packed(const Dims& d, const void* h, const int32_t* offsets,
                                   const void* p2, void* ys, hipStream_t st);
+// the backward input part over packed transposed weights (bf16): W2^T and W13^T in the
+// down layout, dh -> [da|du] and dx_sorted = [da|du] W13
+hipError_t launch_pack_weights_t(const Dims& d, const void* w13, const void* w2, void* p13t,
+                                 void* p2t, hipStream_t st);
+hipError_t launch_ffn_bwd_input_packed(const Dims& d, const int32_t* offsets, const void* p13t,
+                                       const void* p2t, const void* au, const void* dys,
+                                       void* dau, void* dxs, hipStream_t st);
 // FP8 expert GEMMs over packed weight codes (gemm_packed_fp8.hip)
 hipError_t launch_pack_weights_fp8(const Dims& d, const void* w13, const void* w2, void* p13,
                                    void* p2, hipStream_t st);

@@ -71,16 +71,52 @@ __global__ void k_pack_bf16(const uint4* __restrict__ w, uint4* __restrict__ p, 
   }
 }
 
+// The backward input part contracts over the OUTER dimension of the stored weights
+// (dh = dY W2[g] over H, dx = [da|du] W13[g] over 2I), so it gets packed copies of the
+// transposed matrices: B = W[g]^T, with W[g] stored [Kd rows][Nout columns], in the down
+// layout (Nout rows in blocks of 64, k steps of 64 over Kd).  One thread per 16-byte
+// chunk; its 8 elements are W[g][k .. k+7][r], and the 32 lanes of a half-wave take 32
+// consecutive r.
+__global__ void k_pack_bf16_t(const uint16_t* __restrict__ w, uint4* __restrict__ p,
+                              int64_t chunks, int nblk, int nk, int Kd, int Nout) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < chunks; q += stride) {
+    const int l = (int)(q & 63);
+    const int i = (int)((q >> 6) & 7);
+    const int64_t rest = q >> 9;  // (g * nblk + b) * nk + kt
+    const int kt = (int)(rest % nk);
+    const int64_t gb = rest / nk;
+    const int b = (int)(gb % nblk);
+    const int64_t g = gb / nblk;
+    const int n = i >> 2, s = i & 3, c = l & 31, h = l >> 5;
+    const int r = 64 * b + 32 * n + c;
+    const int k = 64 * kt + 16 * s + 8 * h;
+    const uint16_t* src = w + (g * Kd + k) * Nout + r;
+    uint32_t u[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      u[e] = (uint32_t)src[(int64_t)(2 * e) * Nout] |
+             ((uint32_t)src[(int64_t)(2 * e + 1) * Nout] << 16);
+    p[q] = make_uint4(u[0], u[1], u[2], u[3]);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // one tile, MS subtiles of 32 rows, D weight steps in flight
 // ---------------------------------------------------------------------------
-template <bool kSwiglu, int MS, int D>
+// Mode 0: gate/up + SwiGLU (C = h; au: the pre-activations kept for the backward, or
+// NULL).  Mode 1: down (C = Y [rows, Nout]).  Mode 2: the backward's dh, a down-form
+// product over packed W2^T, whose epilogue turns dh into da = dh u silu'(a) and
+// du = dh silu(a) with a = au[r][c], u = au[r][I + c] (I = Nout) and writes both into
+// C = [da|du] [rows, 2I].
+template <int Mode, int MS, int D>
 __device__ __forceinline__ void pk_tile(const uint16_t* __restrict__ A,
                                         const int32_t* __restrict__ gather, int a_rows,
                                         const uint16_t* __restrict__ Bw, bool w_on,
                                         uint16_t* __restrict__ C, uint16_t* __restrict__ au,
                                         int Kd, int Nout, int col0, int64_t grow0, int m_rows,
                                         char* smem, uint32_t lds0, char* stg) {
+  constexpr bool kSwiglu = Mode == 0;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nk = Kd / PBK;
@@ -219,6 +255,59 @@ __device__ __forceinline__ void pk_tile(const uint16_t* __restrict__ A,
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  } else if constexpr (Mode == 2) {
+    // as the down epilogue below, twice per subtile: the da columns, then the du columns
+    const int r = lane & 31;
+    const int I = Nout;
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+      const bool live = 32 * m + r < m_rows;
+      const uint16_t* ar = au + (grow0 + 32 * m + r) * 2 * I + col0 + 4 * (lane >> 5);
+      float da[2][16], du[2][16];
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 av = make_uint2(0u, 0u), uv = make_uint2(0u, 0u);
+          if (live) {
+            av = *reinterpret_cast<const uint2*>(ar + 32 * n + 8 * q);
+            uv = *reinterpret_cast<const uint2*>(ar + I + 32 * n + 8 * q);
+          }
+          const uint32_t aw[2] = {av.x, av.y}, uw[2] = {uv.x, uv.y};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t ab = (t & 1) ? (aw[t >> 1] & 0xFFFF0000u) : (aw[t >> 1] << 16);
+            const uint32_t ub = (t & 1) ? (uw[t >> 1] & 0xFFFF0000u) : (uw[t >> 1] << 16);
+            const float a = __uint_as_float(ab), u = __uint_as_float(ub);
+            const float dh = acc[m][n][4 * q + t];
+            const float sg = 1.0f / (1.0f + __expf(-a));
+            da[n][4 * q + t] = dh * u * (sg * (1.0f + a * (1.0f - sg)));
+            du[n][4 * q + t] = dh * (a * sg);
+          }
+        }
+      const int nrows = min(32, m_rows - 32 * m);
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float* v4 = part ? &du[n][4 * q] : &da[n][4 * q];
+            const int j = 4 * n + q;
+            *reinterpret_cast<uint2*>(stg + r * 128 + ((j ^ (r & 7)) << 4) + (lane >> 5) * 8) =
+                pack4_bf16(v4[0], v4[1], v4[2], v4[3]);
+          }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int fr = 8 * p + (lane >> 3), j = lane & 7;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(stg + fr * 128 + ((j ^ (fr & 7)) << 4));
+          if (fr < nrows)
+            __builtin_nontemporal_store(
+                v, reinterpret_cast<u32x4*>(C + (grow0 + 32 * m + fr) * 2 * I + part * I + col0 +
+                                            8 * j));
+        }
+      }
+    }
   } else {
     // lane: row 32m + l%32, columns col0 + 32n + 8q + 4(l/32) .. +3 (4 per group q of
     // four elements).  Each 32-row subtile is staged in the wave's own 4 KiB of LDS
@@ -250,8 +339,9 @@ __device__ __forceinline__ void pk_tile(const uint16_t* __restrict__ A,
 }
 
 // gather != nullptr: row r of the permuted order is row gather[r] of A (a_rows rows).
-// kSwiglu: Nout = I (h columns), Bp = packed W13; else Nout = H, Bp = packed W2.
-template <bool kSwiglu>
+// Mode 0: Nout = I (h columns), Bp = packed W13.  Mode 1: Nout = H, Bp = packed W2.
+// Mode 2: Nout = I, Bp = packed W2^T, A = dY, au the saved pre-activations (read).
+template <int Mode>
 __global__ __launch_bounds__(256, 1) void k_gemm_packed(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ Bp,
                                                         uint16_t* __restrict__ C,
@@ -259,6 +349,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_packed(const uint16_t* __restri
                                                         const int32_t* __restrict__ gather,
                                                         uint16_t* __restrict__ au, int a_rows,
                                                         int NG, int Kd, int Nout) {
+  constexpr bool kSwiglu = Mode == 0;
   __shared__ __attribute__((aligned(1024))) char smem[kPRing + 4 * kPStg];
   __shared__ int mt_start[kMaxGroups + 1];
   // the cost prefix is only needed for the XCD split below, before the first tile's
@@ -301,10 +392,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_packed(const uint16_t* __restri
 #define PK_CASE(MSV)                                                                      \
   case MSV:                                                                               \
     if (deep && MSV <= 4)                                                                 \
-      pk_tile<kSwiglu, MSV, 3>(A, gather, a_rows, Bw, w_on, C, au, Kd, Nout, col0, grow0, \
+      pk_tile<Mode, MSV, 3>(A, gather, a_rows, Bw, w_on, C, au, Kd, Nout, col0, grow0,    \
                                m_rows, smem, lds0, stg);                                  \
     else                                                                                  \
-      pk_tile<kSwiglu, MSV, 1>(A, gather, a_rows, Bw, w_on, C, au, Kd, Nout, col0, grow0, \
+      pk_tile<Mode, MSV, 1>(A, gather, a_rows, Bw, w_on, C, au, Kd, Nout, col0, grow0,    \
                                m_rows, smem, lds0, stg);                                  \
     break;
     switch (ms) {
@@ -371,7 +462,7 @@ hipError_t launch_ffn_up_packed(const Dims& d, const void* xs, const int32_t* of
         static_cast<uint16_t*>(h) + r0 * d.I, aua, (int)d.T, d.H, d.I, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_gemm_packed<true>, dim3(pk_grid()), dim3(256), 0, st,
+  hipLaunchKernelGGL(k_gemm_packed<0>, dim3(pk_grid()), dim3(256), 0, st,
                      static_cast<const uint16_t*>(xs), static_cast<const uint16_t*>(p13),
                      static_cast<uint16_t*>(h), offsets, gather, static_cast<uint16_t*>(au),
                      (int)d.T, ng, d.H, d.I);
@@ -380,9 +471,50 @@ hipError_t launch_ffn_up_packed(const Dims& d, const void* xs, const int32_t* of
 
 hipError_t launch_ffn_down_packed(const Dims& d, const void* h, const int32_t* offsets,
                                   const void* p2, void* ys, hipStream_t st) {
-  hipLaunchKernelGGL(k_gemm_packed<false>, dim3(pk_grid()), dim3(256), 0, st,
+  hipLaunchKernelGGL(k_gemm_packed<1>, dim3(pk_grid()), dim3(256), 0, st,
                      static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(p2),
                      static_cast<uint16_t*>(ys), offsets, nullptr, nullptr, 0, d.E + d.S, d.I,
+                     d.H);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weights_t(const Dims& d, const void* w13, const void* w2, void* p13t,
+                                 void* p2t, hipStream_t st) {
+  const int NG = d.E + d.S;
+  if (w2) {  // W2[g] is [H, I]: its transpose packed as I rows over k = H
+    const int64_t chunks = (int64_t)NG * d.I * d.H / 8;
+    hipLaunchKernelGGL(k_pack_bf16_t, dim3(4096), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(w2), static_cast<uint4*>(p2t), chunks,
+                       d.I / 64, d.H / PBK, d.H, d.I);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (w13) {  // W13[g] is [2I, H]: its transpose packed as H rows over k = 2I
+    const int64_t chunks = (int64_t)NG * 2 * d.I * d.H / 8;
+    hipLaunchKernelGGL(k_pack_bf16_t, dim3(4096), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(w13), static_cast<uint4*>(p13t), chunks,
+                       d.H / 64, 2 * d.I / PBK, 2 * d.I, d.H);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_ffn_bwd_input_packed(const Dims& d, const int32_t* offsets, const void* p13t,
+                                       const void* p2t, const void* au, const void* dys,
+                                       void* dau, void* dxs, hipStream_t st) {
+  const int NG = d.E + d.S;
+  // dh = dY W2 (k over H) -> [da|du]
+  hipLaunchKernelGGL(k_gemm_packed<2>, dim3(pk_grid()), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(dys), static_cast<const uint16_t*>(p2t),
+                     static_cast<uint16_t*>(dau), offsets, nullptr,
+                     const_cast<uint16_t*>(static_cast<const uint16_t*>(au)), 0, NG, d.H, d.I);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dx_sorted = [da|du] W13 (k over 2I)
+  hipLaunchKernelGGL(k_gemm_packed<1>, dim3(pk_grid()), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(dau), static_cast<const uint16_t*>(p13t),
+                     static_cast<uint16_t*>(dxs), offsets, nullptr, nullptr, 0, NG, 2 * d.I,
                      d.H);
   return hipGetLastError();
 }

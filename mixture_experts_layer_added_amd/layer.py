@@ -65,7 +65,9 @@ class MoELayer:
     train=True (bf16 / fp32): the gate/up GEMM also keeps the pre-activations (au) and
     backward(dy) computes dx, dw_router, dw13 and dw2 (weight gradients in fp32).
     packed (bf16 and FP8 experts): the expert GEMMs run over copies of w13 and w2 in the
-    library's packed layout, made once here (bf16: the same results bit for bit).  Default: on when the
+    library's packed layout, made once here (bf16: the same results bit for bit; with
+    train, the backward input part also runs over packed copies of the transposed
+    matrices, the same results bit for bit).  Default: on when the
     mean load per routed expert, T*K/E, is at most PACKED_MAX_MEAN_ROWS -- the packed
     kernels take at most 192 rows of an expert per tile (a larger expert streams its
     weights once per tile), the natural-layout kernels 256.
@@ -86,10 +88,13 @@ class MoELayer:
         self.p = shape.problem()
         self.w_router, self.bias = w_router, bias
         self.w13, self.w2, self.w13_scale, self.w2_scale = w13, w2, w13_scale, w2_scale
-        self.w13p = self.w2p = None
+        self.w13p = self.w2p = self.w13tp = self.w2tp = None
         if self.packed:
             self.w13p, self.w2p = torch.empty_like(w13), torch.empty_like(w2)
             L.moe_pack_expert_weights(self.p, w13, w2, self.w13p, self.w2p)
+            if train and shape.expert == "bf16":  # the backward's transposed copies
+                self.w13tp, self.w2tp = torch.empty_like(w13), torch.empty_like(w2)
+                L.moe_pack_expert_weights_transposed(self.p, w13, w2, self.w13tp, self.w2tp)
         T, H, E, K, R = shape.T, shape.H, shape.E, shape.K, shape.R
         act = torch.float32 if shape.act == "f32" else torch.bfloat16
         dev = torch.device(device)
@@ -212,6 +217,11 @@ class MoELayer:
         L.moe_bias_update(self.p, self.counts, gamma, self.bias, stream)
 
     def expert_ffn_backward_input(self, stream=None):
+        if self.w13tp is not None:
+            L.moe_expert_ffn_backward_input_packed(self.p, self.offsets, self.w13tp, self.w2tp,
+                                                   self.au, self.dy_sorted, self.dau,
+                                                   self.dx_sorted, stream)
+            return
         L.moe_expert_ffn_backward_input(self.p, self.offsets, self.w13, self.w2, self.au,
                                         self.dy_sorted, self.dau, self.dx_sorted, stream)
 

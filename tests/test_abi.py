@@ -273,3 +273,28 @@ def test_packed_entry_points_validate(L):
     assert rc == L.MOE_ERR_INVALID_ARG and "au" in L.last_error()
     rc = lib.moe_expert_ffn_down_packed(ctypes.byref(p8), d, None, d, e, d, d, None)
     assert rc == L.MOE_ERR_INVALID_ARG and "h_scale" in L.last_error()
+
+
+def test_packed_backward_entry_points_validate(L):
+    """The transposed packing and the packed backward input part take bf16 activations
+    and experts only, and reject missing or aliased buffers before touching the device."""
+    lib = L.lib()
+    d, e = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+    p = prob(L, act_dtype=1, expert_dtype=1)
+    for q in (prob(L, act_dtype=1, expert_dtype=2), prob(L, act_dtype=0, expert_dtype=0)):
+        assert lib.moe_pack_expert_weights_transposed(ctypes.byref(q), d, d, e, e, None) == \
+            L.MOE_ERR_UNSUPPORTED
+        assert lib.moe_expert_ffn_backward_input_packed(ctypes.byref(q), d, d, d, d, d, d, d,
+                                                        None) == L.MOE_ERR_UNSUPPORTED
+    rc = lib.moe_pack_expert_weights_transposed(ctypes.byref(p), None, None, e, e, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "both NULL" in L.last_error()
+    rc = lib.moe_pack_expert_weights_transposed(ctypes.byref(p), None, d, None, None, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "packed output" in L.last_error()
+    rc = lib.moe_pack_expert_weights_transposed(ctypes.byref(p), d, None, d, None, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "in place" in L.last_error()
+    rc = lib.moe_expert_ffn_backward_input_packed(ctypes.byref(p), d, None, d, d, d, d, d, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "w13t_packed" in L.last_error()
+    rc = lib.moe_expert_ffn_backward_input_packed(ctypes.byref(p), d, d, d, None, d, d, d, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "au" in L.last_error()
+    rc = lib.moe_expert_ffn_backward_input_packed(ctypes.byref(p), None, d, d, d, d, d, d, None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "offsets" in L.last_error()

@@ -197,3 +197,76 @@ def test_packed_equals_natural_fp8_v3():
         f"rows per expert {counts.min()}..{counts.max()}")
     del pk, nat
     torch.cuda.empty_cache()
+
+
+def packT_np(w):
+    """Packed layout of the transposes W[g]^T for W [NG, Kd, Nout]: the down layout with
+    Nout rows and k over Kd (moe_pack_expert_weights_transposed)."""
+    t = np.ascontiguousarray(w.transpose(0, 2, 1))   # [NG, Nout, Kd]
+    return pack2_np(t, t.shape[2], t.shape[1])
+
+
+@pytest.mark.parametrize("H,I,E,S", [(384, 256, 3, 1), (256, 128, 5, 0)])
+def test_pack_transposed_layout_bitexact(H, I, E, S):
+    from mixture_experts_layer_added_amd import _lib as L
+    rng = np.random.default_rng(3 * H + I + E)
+    NG = E + S
+    w13 = rng.integers(0, 1 << 16, size=(NG, 2 * I, H), dtype=np.uint16)
+    w2 = rng.integers(0, 1 << 16, size=(NG, H, I), dtype=np.uint16)
+    d13 = torch.from_numpy(w13.view(np.int16)).cuda()
+    d2 = torch.from_numpy(w2.view(np.int16)).cuda()
+    p13, p2 = torch.full_like(d13, -1), torch.full_like(d2, -1)
+    p = L.problem(64, H, E, 1, 1, 1, 1, I, S, L.MOE_BF16, L.MOE_BF16)
+    L.moe_pack_expert_weights_transposed(p, d13, d2, p13, p2)
+    torch.cuda.synchronize()
+    assert np.array_equal(p13.cpu().numpy().view(np.uint16).reshape(NG, H, 2 * I),
+                          packT_np(w13).reshape(NG, H, 2 * I))
+    assert np.array_equal(p2.cpu().numpy().view(np.uint16).reshape(NG, I, H),
+                          packT_np(w2).reshape(NG, I, H))
+
+
+def _bwd_compare(w, x, wr, b, w13, w2, dy, tag):
+    """The backward input part over packed transposed weights against the natural-layout
+    kernels on the same forward: [da|du] and dx_sorted bit-identical."""
+    from mixture_experts_layer_added_amd.layer import MoELayer
+    sh = shape_of(w)
+    pk = MoELayer(sh, wr, b, w13, w2, gather=True, train=True, packed=True)
+    nat = MoELayer(sh, wr, b, w13, w2, gather=True, train=True, packed=False)
+    assert pk.w13tp is not None and nat.w13tp is None
+    for layer in (pk, nat):
+        layer.forward(x)
+        layer.combine_backward(dy)
+        layer.expert_ffn_backward_input()
+    torch.cuda.synchronize()
+    _same(pk.dau, nat.dau, tag + " [da|du]")
+    _same(pk.dx_sorted, nat.dx_sorted, tag + " dx_sorted")
+    counts = np_(pk.counts)
+    return counts
+
+
+@pytest.mark.parametrize("name", ["ragged-bf16", "rows150-bf16", "v3route-bf16", "noshared-bf16",
+                                  "dense-bf16"])
+def test_packed_backward_input_equals_natural_small(name):
+    w = case(name)
+    inp = make_cpu_inputs(w)
+    dev = lambda t: t.contiguous().cuda()  # noqa: E731
+    g = torch.Generator().manual_seed(11)
+    dy = torch.randn((w.T, w.H), generator=g).to(torch.bfloat16)
+    counts = _bwd_compare(w, dev(inp["x"]), dev(inp["w_router"]), dev(inp["bias"]),
+                          dev(inp["w13"]), dev(inp["w2"]), dev(dy), name)
+    log(f"    {name}: backward input part bit-identical; rows per expert "
+        f"{counts.min()}..{counts.max()}")
+
+
+def test_packed_backward_input_equals_natural_v3():
+    w = workloads.get("v3-bf16")
+    dev = torch.device("cuda")
+    wr, b = workloads.make_router(w, dev)
+    w13, w2 = workloads.make_experts(w, dev)
+    x = workloads.make_x(w, device=dev)
+    g = torch.Generator(device=dev).manual_seed(5)
+    dy = torch.randn((w.T, w.H), generator=g, device=dev).to(torch.bfloat16)
+    counts = _bwd_compare(w, x, wr, b, w13, w2, dy, "v3-bf16")
+    log(f"[packed backward vs natural] v3-bf16 T={w.T}: [da|du] [{w.R}x{2 * w.I}] and "
+        f"dx_sorted [{w.R}x{w.H}] bit-identical; rows per expert {counts.min()}..{counts.max()}")
+    torch.cuda.empty_cache()

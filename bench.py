@@ -325,7 +325,7 @@ def main():
         up_tfs = tfs(up_flops, avg_ms["ffn_up"])
         intensity = up_flops / up_bytes
         ridge = MFMA_PEAK[w.expert] * 1e12 / (HBM_PEAK_GBS * 1e9)
-        gk = "k_gemm_packed<true>" if layer.packed else "k_gemm_bf16<true>"
+        gk = "k_gemm_packed<0>" if layer.packed else "k_gemm_bf16<true>"
         if w.expert == "bf16":
             up_name = (f"gate/up GEMM + SwiGLU call: {gk} (routed experts, grouped) + "
                        "k_gemm_dense_swiglu_bf16 (the shared expert, when T >= 2048)")

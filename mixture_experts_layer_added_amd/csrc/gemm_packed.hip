@@ -249,8 +249,9 @@ __device__ __forceinline__ void pk_tile(const uint16_t* __restrict__ A,
         __builtin_nontemporal_store(f32_to_bf16_bits(silu(acc[m][0][e]) * acc[m][1][e]),
                                     cp + (int64_t)row * half);
         if (ap) {  // gate and up pre-activations, kept for the backward
-          ap[(int64_t)row * 2 * half] = f32_to_bf16_bits(acc[m][0][e]);
-          ap[(int64_t)row * 2 * half + half] = f32_to_bf16_bits(acc[m][1][e]);
+          __builtin_nontemporal_store(f32_to_bf16_bits(acc[m][0][e]), ap + (int64_t)row * 2 * half);
+          __builtin_nontemporal_store(f32_to_bf16_bits(acc[m][1][e]),
+                                      ap + (int64_t)row * 2 * half + half);
         }
       }
       __builtin_amdgcn_sched_barrier(0);

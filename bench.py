@@ -332,8 +332,9 @@ def main():
         elif w.expert == "e4m3":
             up_name = ("gate/up GEMM + SwiGLU call (e4m3): "
                        f"{'k_gemm_packed_fp8<true>' if layer.packed else 'k_gemm_fp8<true>'} "
-                       "(routed experts, grouped) + k_gemm_dense_swiglu_fp8 (the shared "
-                       "expert, when T >= 2048)")
+                       "(routed experts, grouped) + k_gemm_dense_swiglu_fp8_w (the shared "
+                       "expert, when T >= 2048; k_gemm_dense_swiglu_fp8 where the wide tiles "
+                       "would not fill the chip)")
         else:
             up_name = "gate/up GEMM + SwiGLU call (fp32): k_gemm_f32<true> (every group)"
         roofline = {"kernel": up_name,

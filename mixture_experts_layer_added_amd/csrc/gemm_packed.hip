@@ -364,7 +364,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_packed(const uint16_t* __restri
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nk = Kd / PBK;
-  const bool deep = (nk & 3) == 0;  // three weight steps in flight need nk % 4 == 0
+  // three weight steps in flight need nk % 4 == 0, and their registers fit beside the
+  // accumulators of up to 4 sub-tiles in the SwiGLU and dh epilogues, of all 6 in down
+  const bool deep = (nk & 3) == 0;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
   char* stg = smem + kPRing + wv * kPStg;
 
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_packed(const uint16_t* __restri
     const int ms = (m_rows + 31) >> 5;
 #define PK_CASE(MSV)                                                                      \
   case MSV:                                                                               \
-    if (deep && MSV <= 4)                                                                 \
+    if (deep && (MSV <= 4 || Mode == 1))                                                 \
       pk_tile<Mode, MSV, 3>(A, gather, a_rows, Bw, w_on, C, au, Kd, Nout, col0, grow0,    \
                                m_rows, smem, lds0, stg);                                  \
     else                                                                                  \

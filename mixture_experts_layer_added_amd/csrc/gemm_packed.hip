@@ -144,9 +144,15 @@ __device__ __forceinline__ void pk_tile(const uint16_t* __restrict__ A,
   u32x4 br[D + 1][8];
   auto bload = [&](int kt, int buf) {
     const uint16_t* p = Bw + (int64_t)kt * kPkStep;
+    // full-height down tiles load their weights through the L2 normally: the shared
+    // expert at a few thousand tokens has many such tiles per weight block, run at
+    // about the same time on one XCD, and the later ones find the block there
+    constexpr bool kTemporal = Mode == 1 && MS == PBM / 32;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      br[buf][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i * 512));
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (kTemporal) br[buf][i] = *reinterpret_cast<const u32x4*>(p + i * 512);
+      else br[buf][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i * 512));
+    }
   };
   f32x16 acc[MS][2];
 #pragma unroll

@@ -141,9 +141,15 @@ __device__ __forceinline__ void pk8_tile(const uint8_t* __restrict__ A,
   u32x4 br[D + 1][4];
   auto bload = [&](int kt, int buf) {
     const uint8_t* p = Bw + (int64_t)kt * kQPStep;
+    // full-height down tiles load their weights through the L2 normally: the shared
+    // expert at a few thousand tokens has many such tiles per weight block, run at
+    // about the same time on one XCD, and the later ones find the block there
+    constexpr bool kTemporal = !kSwiglu && MS == QPM / 32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      br[buf][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i * 1024));
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (kTemporal) br[buf][i] = *reinterpret_cast<const u32x4*>(p + i * 1024);
+      else br[buf][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i * 1024));
+    }
   };
   f32x16 acc[MS];
 #pragma unroll

@@ -440,10 +440,24 @@ __global__ __launch_bounds__(256) void k_router_select(const float* __restrict__
 // r mod G, which re-reads z of its chosen expert for the unbiased affinity; the gate
 // denominator adds the K affinities in rank order.  The one-wave-per-token kernel
 // issued a whole wave's instructions for each token and was bound by that issue; here
-// a wave serves 64/G tokens (V3 shape, T = 262,144: 0.29 instead of 0.74 ms; T = 4096:
-// 20 instead of 33 us; same bits).
+// a wave serves 64/G tokens (V3 shape, T = 262,144: 0.26 instead of 0.74 ms; T = 4096:
+// 19 instead of 33 us; same bits).
 // ---------------------------------------------------------------------------
 constexpr int kLaneMaxGs = 32, kLaneWg = 128;
+
+// DPP lane moves (gfx9 dpp_ctrl codes): quad_perm [1,0,3,2] and [2,3,0,1] (partner at
+// distance 1 and 2 inside a quad), row_half_mirror (lane i of an 8-lane half-row takes
+// lane 7-i) and row_mirror (lane i of a 16-lane row takes lane 15-i)
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppHalfMirror = 0x141,
+              kDppMirror = 0x140;
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<kCtrl>(__float_as_int(v)));
+}
 
 template <int kJ, int kList>
 __global__ __launch_bounds__(kLaneWg) void k_router_select_lanes(
@@ -476,8 +490,9 @@ __global__ __launch_bounds__(kLaneWg) void k_router_select_lanes(
     float zv[kLaneMaxGs];
 #pragma unroll
     for (int c = 0; c < kLaneMaxGs / 4; ++c) {
-      const f32x4 v = __builtin_nontemporal_load(
-          reinterpret_cast<const f32x4*>(zr + e0 + min(4 * c, gs - 4)));
+      // (cached loads: the lanes that keep the K rounds re-read z of their chosen experts
+      // below; streamed past the L2, those re-reads fetched 1.7x the logits' bytes)
+      const f32x4 v = *reinterpret_cast<const f32x4*>(zr + e0 + min(4 * c, gs - 4));
       zv[4 * c] = v[0], zv[4 * c + 1] = v[1], zv[4 * c + 2] = v[2], zv[4 * c + 3] = v[3];
     }
     // list entries: key bits in the low half, expert index in the high half, so an
@@ -525,14 +540,21 @@ __global__ __launch_bounds__(kLaneWg) void k_router_select_lanes(
     for (int r = 0; r < K; ++r) {
       float bv = kept ? key_of(lst[0]) : -__builtin_inff();
       int bi = kept ? idx_of(lst[0]) : 0x7FFFFFFF;
-      for (int off = L >> 1; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, L);
-        const int oi = __shfl_xor(bi, off, L);
+      // the segment's largest (key, index): within 16 lanes by DPP moves (partner in the
+      // quad at distance 1 and 2, then the mirrored lane of the 8- and 16-lane row part),
+      // beyond that by shuffles; any pairing that covers the segment gives every lane
+      // the same maximum of this total order
+      auto take = [&](float ov, int oi) {
         if (ranks_before(ov, oi, bv, bi)) {
           bv = ov;
           bi = oi;
         }
-      }
+      };
+      take(dpp_f<kDppQuadXor1>(bv), dpp_i<kDppQuadXor1>(bi));
+      if (L >= 4) take(dpp_f<kDppQuadXor2>(bv), dpp_i<kDppQuadXor2>(bi));
+      if (L >= 8) take(dpp_f<kDppHalfMirror>(bv), dpp_i<kDppHalfMirror>(bi));
+      if (L >= 16) take(dpp_f<kDppMirror>(bv), dpp_i<kDppMirror>(bi));
+      for (int off = 16; off < L; off <<= 1) take(__shfl_xor(bv, off, L), __shfl_xor(bi, off, L));
       const bool won = kept && idx_of(lst[0]) == bi;
 #pragma unroll
       for (int p = 0; p + 1 < kList; ++p) lst[p] = won ? lst[p + 1] : lst[p];

@@ -435,8 +435,8 @@ __global__ __launch_bounds__(256) void k_router_select(const float* __restrict__
 // the group's keys ordered by (key desc, index asc), and its first J entries give the
 // group score summed from 0 as above.  A group's rank among the token's groups comes
 // from the other lanes' scores by in-segment shuffles; the K rounds then take the
-// largest (key, index) over the heads of the kept lanes' lists with an xor butterfly
-// inside the segment, and the winner's lane drops its head.  Round r is kept by lane
+// largest (key, index) over the heads of the kept lanes' lists with a butterfly of DPP
+// moves inside the segment, and the winner's lane drops its head.  Round r is kept by lane
 // r mod G, which re-reads z of its chosen expert for the unbiased affinity; the gate
 // denominator adds the K affinities in rank order.  The one-wave-per-token kernel
 // issued a whole wave's instructions for each token and was bound by that issue; here

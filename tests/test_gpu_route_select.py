@@ -39,6 +39,9 @@ CASES = {
     "v3-ties": (513, 128, 256, 8, 4, 8, 2, 5),
     "v3-ties-j3": (513, 128, 256, 8, 4, 8, 3, 3),
     "g64-ties": (130, 128, 512, 64, 4, 16, 8, 6),
+    # 16- and 32-lane segments (the rounds' DPP row mirror, then one shuffle stage)
+    "g16-ties": (300, 128, 128, 16, 4, 8, 2, 6),
+    "g32": (200, 128, 256, 32, 8, 12, 3, 0),
     "g8-k16": (200, 128, 128, 8, 3, 16, 4, 0),
 }
 
@@ -80,7 +83,7 @@ def test_select_bitexact(name):
 
 
 def test_select_large_batch():
-    """T = 262,144 at the V3 router shape (the selection's HBM-bound size): the GPU
+    """T = 262,144 at the V3 router shape (the batch the selection is measured at): the GPU
     selection of the GPU logits against the oracle's selection of the same logits."""
     T = 262144
     w = workloads.get("v3-bf16", T=T)

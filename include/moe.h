@@ -117,7 +117,8 @@ moe_status moe_route(const moe_problem* p, const void* x, const float* w_router,
  *                              calls that read the shared rows at T*K + t (the FFN's
  *                              dense shared launch, the combine, the backward) are not
  *                              defined for such input
- *   offsets      [E+S+1] int32 out  first row of each group; offsets[E] = T*K
+ *   offsets      [E+S+1] int32 out  first row of each group; offsets[E] = T*K (for
+ *                                   topk_idx within [0,E), the precondition above)
  *   sorted_token [R]     int32 out  token of each row
  *   inv_perm     [T,K]   int32 out  row holding (t, topk_idx[t,k])
  *   x_sorted     [R,H]   out  act_dtype rows, or FP8 E4M3 codes when expert_dtype is

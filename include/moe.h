@@ -111,7 +111,8 @@ moe_status moe_route(const moe_problem* p, const void* x, const float* w_router,
  * and holds every token in order.
  *   x            [T,H] act_dtype
  *   topk_idx     [T,K] int32   from moe_route; every value must lie in [0,E) (moe_route
- *                              only writes such values).  A pair outside it is skipped
+ *                              only writes such values; moe_count_invalid_ids checks
+ *                              indices of other origin).  A pair outside it is skipped
  *                              and its inv_perm entry is -1 (writes stay in bounds);
  *                              offsets[E] is then T*K less the skipped pairs, and the
  *                              calls that read the shared rows at T*K + t (the FFN's
@@ -133,6 +134,17 @@ moe_status moe_permute(const moe_problem* p, const void* x, const int32_t* topk_
                        int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm,
                        void* x_sorted, float* x_sorted_scale, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* Index check before moe_permute, for callers that build topk_idx themselves
+ * (moe_route only writes values in [0,E)).  Counts the pairs of topk_idx [T,K] (int32,
+ * device) that lie outside [0,E) into n_invalid (one int32 in device memory, owned by
+ * the caller, overwritten; 0 means every pair meets moe_permute's precondition).  Only
+ * enqueues work on `stream`; read the count once the stream has reached it.  With a
+ * nonzero count the caller should not run moe_permute and the calls after it: the
+ * permute skips such pairs and the calls that read the shared rows at T*K + t are then
+ * not defined. */
+moe_status moe_count_invalid_ids(const moe_problem* p, const int32_t* topk_idx,
+                                 int32_t* n_invalid, void* stream);
 
 /* moe_permute without a workspace argument, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid

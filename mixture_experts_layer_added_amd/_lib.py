@@ -23,6 +23,7 @@ EXPORTS = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_up",
            "moe_status_str", "moe_last_error", "moe_expert_ffn_up_save", "moe_combine_backward",
            "moe_router_backward", "moe_expert_ffn_backward_input",
            "moe_expert_ffn_backward_weight", "moe_unpermute_sum", "moe_permute_noalloc",
+           "moe_count_invalid_ids",
            "moe_seq_load_stats", "moe_pack_expert_weights", "moe_expert_ffn_up_packed",
            "moe_expert_ffn_down_packed", "moe_pack_expert_weights_transposed",
            "moe_expert_ffn_backward_input_packed")
@@ -62,6 +63,7 @@ def lib():
         L.moe_route.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_permute.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_permute_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_count_invalid_ids.argtypes = [pp, vp, vp, vp]
         L.moe_seq_load_stats.argtypes = [pp, vp, vp, i32, vp, vp, vp, vp]
         L.moe_expert_ffn.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_expert_ffn_up.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -93,7 +95,8 @@ def lib():
                   "moe_combine", "moe_bias_update", "moe_quantize_weights_fp8",
                   "moe_expert_ffn_up_save", "moe_combine_backward", "moe_router_backward",
                   "moe_expert_ffn_backward_input", "moe_expert_ffn_backward_weight",
-                  "moe_unpermute_sum", "moe_permute_noalloc", "moe_seq_load_stats",
+                  "moe_unpermute_sum", "moe_permute_noalloc", "moe_count_invalid_ids",
+                  "moe_seq_load_stats",
                   "moe_pack_expert_weights", "moe_expert_ffn_up_packed",
                   "moe_expert_ffn_down_packed", "moe_pack_expert_weights_transposed",
                   "moe_expert_ffn_backward_input_packed"):
@@ -149,6 +152,11 @@ def moe_permute(p, x, topk_idx, offsets, sorted_token, inv_perm, x_sorted, x_sor
                              _ptr(sorted_token), _ptr(inv_perm), _ptr(x_sorted),
                              _ptr(x_sorted_scale), _ptr(ws), ws_bytes, _stream(stream)),
            "moe_permute")
+
+
+def moe_count_invalid_ids(p, topk_idx, n_invalid, stream=None):
+    _check(lib().moe_count_invalid_ids(ctypes.byref(p), _ptr(topk_idx), _ptr(n_invalid),
+                                       _stream(stream)), "moe_count_invalid_ids")
 
 
 def moe_permute_noalloc(p, x, topk_idx, offsets, sorted_token, inv_perm, x_sorted,

@@ -179,6 +179,18 @@ moe_status moe_permute(const moe_problem* p, const void* x, const int32_t* topk_
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_permute launch");
 }
 
+moe_status moe_count_invalid_ids(const moe_problem* p, const int32_t* topk_idx,
+                                 int32_t* n_invalid, void* stream) {
+  Dims d;
+  moe_status s = validate(p, &d);
+  if (s != MOE_OK) return s;
+  REQUIRE_PTR(topk_idx);
+  REQUIRE_PTR(n_invalid);
+  if ((s = check_device(nullptr)) != MOE_OK) return s;
+  const hipError_t e = launch_count_invalid(d, topk_idx, n_invalid, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_count_invalid_ids launch");
+}
+
 moe_status moe_permute_noalloc(const moe_problem* p, const void* x, const int32_t* topk_idx,
                                int32_t* offsets, int32_t* sorted_token, int32_t* inv_perm,
                                void* x_sorted, float* x_sorted_scale, void* stream) {

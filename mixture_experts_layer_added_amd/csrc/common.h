@@ -188,6 +188,9 @@ size_t permute_ws_bytes(const Dims& d);
 // address on the current device (looked up once per device).
 size_t permute_scratch_capacity();
 hipError_t permute_scratch(void** ptr);
+// pairs of idx [T,K] outside [0,E), counted into *n_invalid (cleared first)
+hipError_t launch_count_invalid(const Dims& d, const int32_t* idx, int32_t* n_invalid,
+                                hipStream_t st);
 // x_sorted == nullptr: only offsets, sorted_token and inv_perm are written
 hipError_t launch_permute(const Dims& d, const void* x, const int32_t* idx, int32_t* offsets,
                           int32_t* sorted_token, int32_t* inv_perm, void* x_sorted,

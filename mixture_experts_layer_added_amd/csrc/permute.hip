@@ -270,6 +270,38 @@ hipError_t permute_scratch(void** ptr) {
   return hipSuccess;
 }
 
+namespace {
+
+__global__ void k_zero_i32(int32_t* __restrict__ p) { *p = 0; }
+
+// Pairs outside [0,E): each wave counts its lanes' with a ballot and adds the wave's
+// count once (grid-stride over the T*K pairs).
+__global__ __launch_bounds__(256) void k_count_invalid(const int32_t* __restrict__ idx,
+                                                       int64_t n, int E,
+                                                       int32_t* __restrict__ n_invalid) {
+  int cnt = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int e = idx[i];
+    cnt += (e < 0 || e >= E) ? 1 : 0;
+  }
+  // wave sum by shuffles, then one atomic per wave
+  for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+  if ((threadIdx.x & 63) == 0 && cnt) atomicAdd(n_invalid, cnt);
+}
+
+}  // namespace
+
+hipError_t launch_count_invalid(const Dims& d, const int32_t* idx, int32_t* n_invalid,
+                                hipStream_t st) {
+  const int64_t n = d.T * d.K;
+  // the clear is a kernel, not a memset, so the pair can sit in a captured graph
+  hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(1), 0, st, n_invalid);
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4 * device_cu_count());
+  hipLaunchKernelGGL(k_count_invalid, dim3((unsigned)blocks), dim3(256), 0, st, idx, n, d.E,
+                     n_invalid);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const Dims& d, const void* x, const int32_t* idx, int32_t* offsets,
                           int32_t* sorted_token, int32_t* inv_perm, void* x_sorted,
                           float* x_scale, void* ws, hipStream_t st) {

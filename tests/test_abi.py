@@ -218,6 +218,19 @@ def test_noalloc_permute_rejects_problems_beyond_its_scratch(L):
     assert rc == L.MOE_ERR_INVALID_ARG
 
 
+def test_count_invalid_ids_validates(L):
+    """The index check rejects a missing or misaligned pointer and an invalid problem
+    before launching anything."""
+    lib = L.lib()
+    dummy = ctypes.c_void_p(4096)
+    p = prob(L)
+    for args in ((None, dummy), (dummy, None), (ctypes.c_void_p(4100), dummy)):
+        rc = lib.moe_count_invalid_ids(ctypes.byref(p), *args, None)
+        assert rc == L.MOE_ERR_INVALID_ARG
+    bad = prob(L, G=3)  # E % G != 0
+    assert lib.moe_count_invalid_ids(ctypes.byref(bad), dummy, dummy, None) == L.MOE_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("n_seq", [0, -1, (1 << 24) + 1])
 def test_seq_load_stats_rejects_bad_sequence_counts(L, n_seq):
     lib = L.lib()
